@@ -1,0 +1,164 @@
+"""Each pin must fail when a plausible mistake is planted in the oracle.
+
+The mistakes are planted on the CPU by swapping an oracle function for a
+subtly wrong copy; the pin tests are then re-run against it.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_oracle as om
+import test_oracle_assign as ta
+import test_oracle_capacity as tc
+import test_oracle_forward as tf
+import test_oracle_router as tr
+
+
+def _fails(fn, *a):
+    try:
+        fn(*a)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_float_capacity_is_caught(monkeypatch):
+    real = om.capacity_plan
+
+    def float_caps(T, top_k, E, P, W, send_cap=(11, 10), recv_cap=(23, 20), cap_send_rows=0, cap_recv_rows=0):
+        p = real(T, top_k, E, P, W, send_cap, recv_cap, cap_send_rows, cap_recv_rows)
+        p["cap_send"] = math.ceil(send_cap[0] / send_cap[1] * p["Tw"] * top_k / P)
+        return p
+    monkeypatch.setattr(oracle, "capacity_plan", float_caps)
+    assert _fails(tc.test_exact_rational_not_float)
+
+
+def test_floor_instead_of_ceil_is_caught(monkeypatch):
+    real = om.capacity_plan
+
+    def floor_caps(*a, **k):
+        p = real(*a, **k)
+        p["cap_recv"] = math.floor(Fraction(23, 20) * Fraction(p["Tw"] * a[1], a[2]))
+        return p
+    monkeypatch.setattr(oracle, "capacity_plan", floor_caps)
+    assert _fails(tc.test_recv_share_printed_capacity)
+
+
+def test_high_index_tie_break_is_caught(monkeypatch):
+    def bad_topk(l, b, k):
+        s = om.selection_scores(l, b).astype(np.float64)
+        T, E = s.shape
+        idx = np.broadcast_to(np.arange(E), (T, E))
+        return np.lexsort((-idx, -s), axis=-1)[:, :k]
+    monkeypatch.setattr(oracle, "route_topk", bad_topk)
+    assert _fails(tr.test_topk_bruteforce_with_ties, 0)
+    assert _fails(tr.test_all_equal_logits_pick_lowest_indices)
+
+
+def test_fp64_score_is_caught(monkeypatch):
+    def bad_topk(l, b, k):
+        s = np.asarray(l, np.float64) + np.asarray(b, np.float64)[None, :]
+        T, E = s.shape
+        idx = np.broadcast_to(np.arange(E), (T, E))
+        return np.lexsort((idx, -s), axis=-1)[:, :k]
+    monkeypatch.setattr(oracle, "route_topk", bad_topk)
+    assert _fails(tr.test_selection_decided_in_fp32)
+
+
+def test_biased_gates_are_caught(monkeypatch):
+    def bad_gates(l, idx):
+        sel = np.take_along_axis(np.asarray(l, np.float64), idx, axis=1)
+        sel = sel + 0.01 * np.arange(idx.shape[1])   # a stray additive term
+        ex = np.exp(sel - sel.max(1, keepdims=True))
+        return ex / ex.sum(1, keepdims=True)
+    monkeypatch.setattr(oracle, "gates", bad_gates)
+    assert _fails(tr.test_gates_closed_forms)
+
+
+def test_receiver_cap_first_is_caught(monkeypatch):
+    real = om.assign_slots
+
+    def recv_first(idx, E, P, W, cs, cr):
+        # wrong order: the receiver cap is checked first, so a row the
+        # receiver would refuse never takes a pool slot
+        idx = np.asarray(idx)
+        T, k = idx.shape
+        epp = E // P
+        a = real(idx, E, P, W, cs, cr)
+        ps = np.full((T, k), -1)
+        rs = np.full((T, k), -1)
+        for t0, t1 in om.wave_ranges(T, W):
+            pc, ec = [0] * P, [0] * E
+            for t in range(t0, t1):
+                for j in range(k):
+                    e = int(idx[t, j])
+                    p = e // epp
+                    if ec[e] >= cr or pc[p] >= cs:
+                        continue
+                    ps[t, j] = pc[p]
+                    pc[p] += 1
+                    rs[t, j] = ec[e]
+                    ec[e] += 1
+        a["pool_slot"], a["recv_slot"] = ps, rs
+        return a
+    monkeypatch.setattr(oracle, "assign_slots", recv_first)
+    assert _fails(ta.test_brute_force_tiny, 0, 16, 4, 2, 3)
+
+
+def test_global_counters_across_waves_are_caught(monkeypatch):
+    def one_wave(idx, E, P, W, cs, cr):
+        # wrong: counters not reset per wave (waves ignored)
+        return om.assign_slots(idx, E, P, 1, cs, cr) if W == 1 else _reshape(om.assign_slots(idx, E, P, 1, cs, cr), W)
+
+    def _reshape(a, W):
+        a = dict(a)
+        a["pool_count"] = np.repeat(a["pool_count"], W, axis=0)
+        a["expert_count"] = np.repeat(a["expert_count"], W, axis=0)
+        a["bank_rows"] = np.repeat(a["bank_rows"], W, axis=0)
+        a["ids"] = np.repeat(a["ids"], W, axis=0)
+        return a
+    monkeypatch.setattr(oracle, "assign_slots", one_wave)
+    assert _fails(ta.test_waves_are_independent_chunks)
+
+
+def test_renormalised_gates_are_caught(monkeypatch):
+    real = om.combine
+
+    def renorm(g, recv_slot, o):
+        keep = (np.asarray(recv_slot) >= 0)
+        g = np.asarray(g) * keep
+        s = g.sum(1, keepdims=True)
+        g = np.where(s > 0, g / np.where(s > 0, s, 1), 0)
+        return real(g, recv_slot, o)
+    monkeypatch.setattr(om, "combine", renorm)
+    assert _fails(tf.test_combine_then_project_is_project_then_combine)
+
+
+def test_transposed_weight_is_caught(monkeypatch):
+    def bad_swiglu(u, wg, wu, wd):
+        u = np.asarray(u, np.float64)
+        return (om.silu(u @ np.asarray(wg).T) * (u @ np.asarray(wu).T)) @ np.asarray(wd).reshape(np.asarray(wd).T.shape)
+    monkeypatch.setattr(om, "swiglu", bad_swiglu)
+    monkeypatch.setattr(oracle, "swiglu", bad_swiglu)
+    assert _fails(tf.test_swiglu_matches_library)
+    assert _fails(tf.test_single_expert_is_a_dense_mlp_stack)
+
+
+def test_wrong_pool_map_is_caught(monkeypatch):
+    real = om.assign_slots
+
+    def strided_pools(idx, E, P, W, cs, cr):
+        # wrong map e -> e mod P, emulated by relabelling experts
+        idx = np.asarray(idx)
+        perm = np.array([(e % P) * (E // P) + e // P for e in range(E)])
+        a = real(perm[idx], E, P, W, cs, cr)
+        inv = np.argsort(perm)
+        a["ids"] = np.where(a["ids"] >= 0, inv[np.maximum(a["ids"], 0)], -1)
+        a["expert_count"] = a["expert_count"][:, perm]
+        a["bank_rows"] = a["bank_rows"][:, perm]
+        return a
+    monkeypatch.setattr(oracle, "assign_slots", strided_pools)
+    assert _fails(ta.test_closed_forms_tiny_workload, 0)
