@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the pooled-wave MoE branch forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload marin_16k]
+
+A step is one moe_forward call (latent projection, router, top-k, pooled
+dispatch with both caps, receiver binning, grouped SwiGLU experts, combine,
+up-projection and shared experts) over one batch of seeded synthetic inputs
+already resident in HBM.  Prints one JSON line.
+
+Stage durations come from HIP events the library records between its kernel
+launches on the stream it launches them on (moe_forward_profiled), averaged
+over the timed steps.  The dominant kernel's roofline fraction uses
+algorithmic flops or bytes per launch (kept rows only, never padded
+capacity).  The CPU baseline times the fp64 oracle on a bounded token sample
+of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; % bf16 MFMA peak; drop fraction"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+def stage_work(w, kept, sent):
+    """Algorithmic flops (MFMA stages) or bytes (HBM stages) per launch."""
+    eb = 2 if w.dtype == "bf16" else 4
+    T, D, L, E, k, F = w.T, w.d_model, w.d_latent, w.n_experts, w.top_k, w.d_ff
+    S, Fs = w.n_shared, w.d_ff_shared
+    return {
+        "latent": ("mfma", 2.0 * T * D * L),
+        "router": ("mfma", 2.0 * T * L * E),
+        "topk": ("hbm", T * E * 4 + T * k * 8),
+        "assign": ("hbm", T * k * 4 + 2 * T * k * 4 + sent * 4),
+        "scatter": ("hbm", T * L * eb + sent * L * eb + 2 * T * k * 4),
+        "recv_bin": ("hbm", 0.0),
+        "expert_rows": ("hbm", 0.0),
+        "expert_gate_up": ("mfma", 2.0 * kept * L * 2 * F),
+        "expert_down": ("mfma", 2.0 * kept * F * L),
+        "combine": ("hbm", kept * L * eb + T * L * eb + 4 * T * k * 4),
+        "shared_gate_up": ("mfma", 2.0 * T * D * 2 * S * Fs),
+        "output": ("mfma", 2.0 * T * D * (L + S * Fs)),
+    }
+
+
+def cpu_baseline(w, inp, n_tok):
+    """The fp64 oracle on the first n_tok tokens (its own batch: caps are
+    derived for n_tok tokens), weights given as the run's bf16 values."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 0) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [0])
+    except Exception:  # threadpoolctl missing: report the affinity mask
+        blas_threads = 0
+    cores = len(os.sched_getaffinity(0))
+
+    def f64(t):
+        return t.detach().to("cpu").to(torch.float64).numpy()
+    x = f64(inp["x"][:n_tok])
+    wt = {k: f64(inp[k]) for k in ("w_latent", "w_router", "w_up_proj", "ws_gate", "ws_up",
+                                   "ws_down")}
+    wt["router_bias"] = inp["router_bias"].cpu().numpy().astype(np.float32)
+    host = {k: inp[k].cpu() for k in ("w_gate", "w_up", "w_down")}   # bf16 on the host
+    wt["expert_weights"] = lambda e: (host["w_gate"][e].to(torch.float64).numpy(),
+                                      host["w_up"][e].to(torch.float64).numpy(),
+                                      host["w_down"][e].to(torch.float64).numpy())
+    t0 = time.perf_counter()
+    r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
+                       send_cap=w.send_cap, recv_cap=w.recv_cap)
+    dt = time.perf_counter() - t0
+    assert r["y"].shape == (n_tok, w.d_model)
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": blas_threads or cores,
+            "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the {w.name} inputs as their own batch "
+                      f"(caps for {n_tok} tokens), fp64 numpy, {dt:.1f} s wall, "
+                      f"{cores} cores in the affinity mask"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="marin_16k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch of the dominant kernel (JSON)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import routing_capacity_dispatch_amd as rcd
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    cfg = rcd.config_of(w)
+    print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w, args.seed, device=dev)
+    x = inp["x"]
+    fwd = rcd.Forward(cfg, {k: v for k, v in inp.items() if k != "x"}, dev)
+    nst = rcd.stage_count()
+    stages = rcd.abi.STAGES
+    assert len(stages) == nst
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fwd(x)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    for row in ev:       # torch creates its events lazily, on first record
+        for e in row:
+            e.record()
+    print(f"# timing {K} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        fwd.profiled(x, ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / K
+
+    per = {s: 0.0 for s in stages}
+    for i in range(K):
+        for j, s in enumerate(stages):
+            per[s] += ev[i][j].elapsed_time(ev[i][j + 1]) / K
+    kept, sd, rd = [int(v) for v in fwd.counts.cpu().tolist()]
+    sent = kept + rd
+    work = stage_work(w, kept, sent)
+    peak_f = PEAK_TFLOPS[w.dtype]
+    st_out = {}
+    for s in stages:
+        kind, amount = work[s]
+        ms = per[s]
+        if kind == "mfma":
+            ach = amount / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+            st_out[s] = {"ms": round(ms, 4), "tflops": round(ach, 1),
+                         "frac_peak": round(ach / peak_f, 4)}
+        else:
+            ach = amount / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+            st_out[s] = {"ms": round(ms, 4), "gbs": round(ach, 1),
+                         "frac_peak": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(stages, key=lambda s: per[s])
+    kind, amount = work[dom]
+    if kind == "mfma":
+        ach = amount / (per[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_f, "unit": "TFLOP/s",
+                "frac": round(ach / peak_f, 4)}
+    else:
+        ach = amount / (per[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    if args.traffic and os.path.exists(args.traffic):
+        try:
+            tr = json.load(open(args.traffic))
+            if tr.get("kernel") == dom and tr.get("workload") == w.name:
+                roof["traffic"] = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            pass
+    gemm_flops = sum(work[s][1] for s in stages if work[s][0] == "mfma")
+    gemm_ms = sum(per[s] for s in stages if work[s][0] == "mfma")
+    tokens_s = w.T / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_latent": w.d_latent,
+                   "n_experts": w.n_experts, "n_pools": w.n_pools, "top_k": w.top_k,
+                   "d_ff": w.d_ff, "n_shared": w.n_shared, "d_ff_shared": w.d_ff_shared,
+                   "n_waves": w.n_waves, "caps": [list(w.send_cap), list(w.recv_cap)],
+                   "global_batch": w.T, "parallelism": "single GPU"},
+        "roofline": roof,
+        "gemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_f, 4),
+        "drop_fraction": {"sender": sd / (w.T * w.top_k), "receiver": rd / (w.T * w.top_k),
+                          "total": (sd + rd) / (w.T * w.top_k)},
+        "stages": st_out,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print(f"# cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+"""Pooled-wave capacity-dispatch MoE branch (forward) for MI355X / gfx950.
+
+Thin torch binding over the C ABI in include/moe.h (libmoe.so).  torch only
+provides device memory and the current stream; every step of the branch runs
+in the HIP kernels of the library.  The same names as the C entry points:
+route, dispatch, experts, combine, forward, plus make_config / plan.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Dict, Optional
+
+import torch
+
+from . import abi
+
+__all__ = ["make_config", "plan", "route", "dispatch", "experts", "combine", "forward",
+           "library", "MoeError"]
+
+MoeError = abi.MoeError
+_DT = {"f32": abi.MOE_F32, "bf16": abi.MOE_BF16, torch.float32: abi.MOE_F32,
+       torch.bfloat16: abi.MOE_BF16}
+
+
+def library():
+    return abi.load()
+
+
+def make_config(T, d_model, d_latent, n_experts, n_pools, top_k, d_ff, n_shared=0,
+                d_ff_shared=0, n_waves=3, dtype="bf16", send_cap=(11, 10), recv_cap=(23, 20),
+                cap_send_rows=0, cap_recv_rows=0) -> abi.MoeConfig:
+    return abi.MoeConfig(
+        T=T, d_model=d_model, d_latent=d_latent, n_experts=n_experts, n_pools=n_pools,
+        top_k=top_k, d_ff=d_ff, n_shared=n_shared, d_ff_shared=d_ff_shared, n_waves=n_waves,
+        send_cap_num=send_cap[0], send_cap_den=send_cap[1], recv_cap_num=recv_cap[0],
+        recv_cap_den=recv_cap[1], cap_send_rows=cap_send_rows, cap_recv_rows=cap_recv_rows,
+        dtype=_DT[dtype], reserved=0)
+
+
+def config_of(w, **over) -> abi.MoeConfig:
+    """Config from any object with the workload attribute names."""
+    f = dict(T=w.T, d_model=w.d_model, d_latent=w.d_latent, n_experts=w.n_experts,
+             n_pools=w.n_pools, top_k=w.top_k, d_ff=w.d_ff, n_shared=w.n_shared,
+             d_ff_shared=w.d_ff_shared, n_waves=w.n_waves, dtype=w.dtype,
+             send_cap=tuple(w.send_cap), recv_cap=tuple(w.recv_cap),
+             cap_send_rows=getattr(w, "cap_send_rows", 0),
+             cap_recv_rows=getattr(w, "cap_recv_rows", 0))
+    f.update(over)
+    return make_config(**f)
+
+
+def plan(cfg: abi.MoeConfig) -> Dict[str, int]:
+    p = abi.MoePlan()
+    abi.check("moe_make_plan", library().moe_make_plan(C.byref(cfg), C.byref(p)))
+    return p.as_dict()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _tdt(cfg):
+    return torch.bfloat16 if cfg.dtype == abi.MOE_BF16 else torch.float32
+
+
+def _ws(nbytes, device):
+    # 256-byte aligned: torch's caching allocator returns 512-byte aligned blocks
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def route(cfg, logits: torch.Tensor, bias: Optional[torch.Tensor] = None, out=None):
+    T, k = cfg.T, cfg.top_k
+    dev = logits.device
+    topk = out["topk_idx"] if out else torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = out["gates"] if out else torch.empty((T, k), dtype=torch.float32, device=dev)
+    abi.check("moe_route", library().moe_route(
+        C.byref(cfg), _ptr(logits), _ptr(bias), _ptr(topk), _ptr(gates), _stream(dev)))
+    return topk, gates
+
+
+def dispatch(cfg, topk_idx: torch.Tensor, z: torch.Tensor) -> Dict[str, torch.Tensor]:
+    p = plan(cfg)
+    dev = z.device
+    T, k, W, P, E = cfg.T, cfg.top_k, cfg.n_waves, cfg.n_pools, cfg.n_experts
+    out = dict(
+        pools=torch.empty(p["pools_bytes"], dtype=torch.uint8, device=dev),
+        pool_slot=torch.empty((T, k), dtype=torch.int32, device=dev),
+        recv_slot=torch.empty((T, k), dtype=torch.int32, device=dev),
+        bank_rows=torch.full((W, E, max(p["cap_recv"], 0)), -1, dtype=torch.int32, device=dev),
+        pool_count=torch.empty((W, P), dtype=torch.int32, device=dev),
+        expert_count=torch.empty((W, E), dtype=torch.int32, device=dev),
+        counts=torch.empty(3, dtype=torch.int64, device=dev),
+    )
+    ws = _ws(p["dispatch_ws_bytes"], dev)
+    abi.check("moe_dispatch", library().moe_dispatch(
+        C.byref(cfg), _ptr(topk_idx), _ptr(z), _ptr(out["pools"]), _ptr(out["pool_slot"]),
+        _ptr(out["recv_slot"]), _ptr(out["bank_rows"]), _ptr(out["pool_count"]),
+        _ptr(out["expert_count"]), _ptr(out["counts"]), _ptr(ws), ws.numel(), _stream(dev)))
+    out["plan"] = p
+    return out
+
+
+def pool_views(cfg, pools: torch.Tensor):
+    """(rows [W, P, C_send, L], ids [W, P, C_send]) views of a pools buffer."""
+    p = plan(cfg)
+    W, P = cfg.n_waves, cfg.n_pools
+    cs, blk = p["cap_send"], p["pool_block_bytes"]
+    if cs == 0:
+        return (torch.empty((W, P, 0, cfg.d_latent), dtype=_tdt(cfg), device=pools.device),
+                torch.empty((W, P, 0), dtype=torch.int32, device=pools.device))
+    b = pools.view(W, P, blk)
+    rows = b[:, :, :p["ids_offset"]].view(_tdt(cfg)).view(W, P, cs, cfg.d_latent)
+    ids = b[:, :, p["ids_offset"]:p["ids_offset"] + 4 * cs].view(torch.int32).view(W, P, cs)
+    return rows, ids
+
+
+def experts(cfg, pools, bank_rows, expert_count, w_gate, w_up, w_down, expert_out=None):
+    p = plan(cfg)
+    dev = pools.device
+    if expert_out is None:
+        expert_out = torch.empty(p["expert_out_bytes"], dtype=torch.uint8, device=dev)
+    ws = _ws(p["experts_ws_bytes"], dev)
+    abi.check("moe_experts", library().moe_experts(
+        C.byref(cfg), _ptr(pools), _ptr(bank_rows), _ptr(expert_count), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(expert_out), _ptr(ws), ws.numel(), _stream(dev)))
+    return expert_out
+
+
+def expert_out_view(cfg, expert_out: torch.Tensor):
+    p = plan(cfg)
+    n = cfg.n_waves * cfg.n_pools * p["cap_send"] * cfg.d_latent
+    return expert_out.view(_tdt(cfg))[:n].view(cfg.n_waves, cfg.n_pools, p["cap_send"],
+                                                 cfg.d_latent)
+
+
+def combine(cfg, expert_out, topk_idx, pool_slot, recv_slot, gates, y_latent=None):
+    dev = expert_out.device
+    if y_latent is None:
+        y_latent = torch.empty((cfg.T, cfg.d_latent), dtype=_tdt(cfg), device=dev)
+    abi.check("moe_combine", library().moe_combine(
+        C.byref(cfg), _ptr(expert_out), _ptr(topk_idx), _ptr(pool_slot), _ptr(recv_slot),
+        _ptr(gates), _ptr(y_latent), _stream(dev)))
+    return y_latent
+
+
+class Forward:
+    """Reusable forward call: weights, workspace and outputs bound once, so a
+    timed loop only enqueues kernels."""
+
+    def __init__(self, cfg, weights: Dict[str, torch.Tensor], device, taps=False):
+        self.cfg = cfg
+        self.p = plan(cfg)
+        self.w = weights
+        self.wstruct = abi.MoeWeights(**{n: _ptr(weights.get(n)) for n, _ in
+                                         abi.MoeWeights._fields_})
+        self.ws = _ws(self.p["forward_ws_bytes"], device)
+        self.y = torch.empty((cfg.T, cfg.d_model), dtype=_tdt(cfg), device=device)
+        self.counts = torch.empty(3, dtype=torch.int64, device=device)
+        self.taps = None
+        self.tap_t = {}
+        if taps:
+            T, k, E, W, P, L = cfg.T, cfg.top_k, cfg.n_experts, cfg.n_waves, cfg.n_pools, cfg.d_latent
+            dt = _tdt(cfg)
+            i32 = dict(dtype=torch.int32, device=device)
+            self.tap_t = dict(
+                logits=torch.empty((T, E), dtype=torch.float32, device=device),
+                topk_idx=torch.empty((T, k), **i32),
+                gates=torch.empty((T, k), dtype=torch.float32, device=device),
+                pool_slot=torch.empty((T, k), **i32),
+                recv_slot=torch.empty((T, k), **i32),
+                pool_count=torch.empty((W, P), **i32),
+                expert_count=torch.empty((W, E), **i32),
+                bank_rows=torch.full((W, E, self.p["cap_recv"]), -1, **i32),
+                z=torch.empty((T, L), dtype=dt, device=device),
+                pools=torch.empty(self.p["pools_bytes"], dtype=torch.uint8, device=device),
+                expert_out=torch.empty(self.p["expert_out_bytes"], dtype=torch.uint8, device=device),
+                y_latent=torch.empty((T, L), dtype=dt, device=device),
+            )
+            self.taps = abi.MoeTaps(**{n: _ptr(t) for n, t in self.tap_t.items()})
+
+    def __call__(self, x: torch.Tensor):
+        lib = library()
+        abi.check("moe_forward", lib.moe_forward(
+            C.byref(self.cfg), C.byref(self.wstruct), _ptr(x), _ptr(self.y),
+            C.byref(self.taps) if self.taps is not None else None, _ptr(self.counts),
+            _ptr(self.ws), self.ws.numel(), _stream(x.device)))
+        return self.y
+
+    def profiled(self, x: torch.Tensor, events):
+        """As __call__, recording torch.cuda.Event objects (enable_timing) at
+        the stage boundaries on the current stream: len(events) ==
+        stage count + 1."""
+        lib = library()
+        arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+        abi.check("moe_forward_profiled", lib.moe_forward_profiled(
+            C.byref(self.cfg), C.byref(self.wstruct), _ptr(x), _ptr(self.y),
+            C.byref(self.taps) if self.taps is not None else None, _ptr(self.counts),
+            _ptr(self.ws), self.ws.numel(), _stream(x.device), arr, len(events)))
+        return self.y
+
+
+def stage_count() -> int:
+    return library().moe_forward_stage_count()
+
+
+def forward(cfg, weights: Dict[str, torch.Tensor], x: torch.Tensor, taps=False):
+    """One forward call; returns (y, counts, taps-dict)."""
+    f = Forward(cfg, weights, x.device, taps=taps)
+    y = f(x)
+    return y, f.counts, f.tap_t

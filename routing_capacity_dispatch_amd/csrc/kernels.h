@@ -1,0 +1,111 @@
+// Internal launchers of the gfx950 kernels (host side).  Each launcher
+// enqueues on `s` and returns hipGetLastError(); shapes are validated by the
+// C-ABI layer before any call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// element types (same values as moe_dtype)
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1 };
+
+// ---------------------------------------------------------------- GEMMs
+// C[M][N] (+)= sum over segments of A_s[M][K_s] * B_s[N][K_s]^T, fp32 accumulate.
+struct GemmSeg {
+  const void* A;
+  int64_t lda;  // elements
+  const void* B;
+  int64_t ldb;  // elements
+  int K;
+};
+constexpr int kMaxSegs = 4;
+struct GemmDense {
+  GemmSeg seg[kMaxSegs];
+  int nseg;
+  void* C;
+  int64_t ldc;  // elements of the output type
+  int M, N;
+};
+// in_dt: element type of A and B; out_dt: element type of C.
+hipError_t launch_gemm_dense(int in_dt, int out_dt, const GemmDense& g, hipStream_t s);
+
+// C[m][g*F + f] = silu(A[m] . Wg[g][f]) * (A[m] . Wu[g][f]) for g < G, f < F
+// (the shared experts; Wg, Wu are [G][F][K]).
+hipError_t launch_swiglu_dense(int dt, const void* A, int64_t lda, const void* Wg,
+                               const void* Wu, int G, int F, int K, int M, void* C,
+                               int64_t ldc, hipStream_t s);
+
+// Routed experts, gate/up half: for expert e and its row m < rows_total[e],
+// u = pool row erow[e][m] (flat (w*P + p)*C_send + s index), and
+// H[e][m][f] = silu(u . Wg[e][f]) * (u . Wu[e][f]).
+struct ExpertGateUp {
+  const char* pools;
+  int64_t block_bytes;
+  int64_t row_bytes;
+  int cap_send;
+  const int32_t* erow;        // [E][max_rows]
+  const int32_t* rows_total;  // [E]
+  int E, max_rows, F, L;
+  const void* Wg;
+  const void* Wu;
+  void* H;  // [E][max_rows][F]
+};
+hipError_t launch_expert_gate_up(int dt, const ExpertGateUp& a, hipStream_t s);
+
+// Routed experts, down half: expert_out row erow[e][m] = H[e][m] . Wd[e]^T.
+struct ExpertDown {
+  const void* H;
+  const int32_t* erow;
+  const int32_t* rows_total;
+  int E, max_rows, F, L;
+  const void* Wd;   // [E][L][F]
+  void* out;        // [W*P*C_send][L]
+};
+hipError_t launch_expert_down(int dt, const ExpertDown& a, hipStream_t s);
+
+// ---------------------------------------------------------------- routing
+hipError_t launch_topk_gates(const float* logits, const float* bias, int64_t T, int E,
+                             int k, int32_t* topk_idx, float* gates, hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch
+struct DispatchArgs {
+  const int32_t* topk;
+  int64_t T;
+  int k, E, P, W;
+  int64_t Tw, cap_send, cap_recv;
+  int32_t* pool_slot;
+  int32_t* recv_slot;
+  int32_t* pool_count;   // [W][P]
+  char* pools;           // block layout
+  int64_t block_bytes, ids_offset, row_bytes;
+  int64_t* wave_counts;  // [W][3] workspace
+  int64_t* counts;       // [3] or null
+};
+hipError_t launch_assign(const DispatchArgs& a, hipStream_t s);
+hipError_t launch_scatter_rows(const DispatchArgs& a, const void* z, hipStream_t s);
+hipError_t launch_recv_bin(const DispatchArgs& a, int32_t* bank_rows,
+                           int32_t* expert_count, hipStream_t s);
+hipError_t launch_expert_rows(const int32_t* bank_rows, const int32_t* expert_count,
+                              int E, int P, int W, int64_t cap_send, int64_t cap_recv,
+                              int32_t* erow, int32_t* rows_total, int max_rows,
+                              hipStream_t s);
+
+// ---------------------------------------------------------------- combine
+struct CombineArgs {
+  const char* expert_out;
+  const int32_t* topk;
+  const int32_t* pool_slot;
+  const int32_t* recv_slot;
+  const float* gates;
+  int64_t T, Tw;
+  int k, E, P;
+  int64_t cap_send, row_bytes;
+  void* y;
+};
+hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s);
+
+hipError_t launch_zero_i64(int64_t* p, int n, hipStream_t s);
+
+}  // namespace moe

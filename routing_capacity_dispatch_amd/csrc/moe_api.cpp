@@ -1,0 +1,448 @@
+// Host side of the C ABI: validation, capacity plan, workspace carving and
+// the launch sequence of the branch.  No allocation, no host synchronisation.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+// Stages of moe_forward, in launch order: latent GEMM, router GEMM, top-k,
+// slot assignment, row scatter, receiver binning, expert row lists, expert
+// gate/up GEMM, expert down GEMM, combine, shared gate/up GEMM, output GEMM.
+constexpr int kStages = 12;
+
+// Records stage boundary i (event i) on the stream when events are given.
+struct Marks {
+  void* const* ev;
+  int n;
+  int next;
+  hipError_t mark(hipStream_t s) {
+    if (!ev || next >= n) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[next++]), s);
+  }
+};
+
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+  char* base;
+  int64_t used;
+  void* take(int64_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += align256(bytes);
+    return p;
+  }
+};
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
+// Sizes every entry point needs.  top_k is the number of assignments per
+// token; only selection (moe_route, moe_forward) also needs top_k <= E.
+moe_status check_route_shape(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->n_experts < 1 || c->top_k < 1) return MOE_ERR_INVALID_ARG;
+  if (c->T * (int64_t)c->n_experts > kI32Max * 64) return MOE_ERR_UNSUPPORTED;
+  if (c->T * (int64_t)c->top_k > kI32Max) return MOE_ERR_INVALID_ARG;
+  if (c->n_experts > 1024 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Capacity with exact integer arithmetic: ceil(num * Tw * k / (den * n)).
+int64_t capacity(int64_t num, int64_t den, int64_t Tw, int64_t k, int64_t n) {
+  const __int128 a = (__int128)num * Tw * k;
+  const __int128 b = (__int128)den * n;
+  return (int64_t)((a + b - 1) / b);
+}
+
+moe_status plan_impl(const moe_config* c, moe_plan* p) {
+  if (!c || !p) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_route_shape(c);
+  if (st != MOE_OK) return st;
+  if (c->d_model < 1 || c->d_latent < 1 || c->d_ff < 1 || c->n_pools < 1 || c->n_waves < 1 ||
+      c->n_shared < 0 || (c->n_shared > 0 && c->d_ff_shared < 1))
+    return MOE_ERR_INVALID_ARG;
+  if (c->n_experts % c->n_pools) return MOE_ERR_INVALID_ARG;
+  if (c->send_cap_num < 0 || c->send_cap_den < 1 || c->recv_cap_num < 0 || c->recv_cap_den < 1 ||
+      c->cap_send_rows < 0 || c->cap_recv_rows < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (c->d_model % 64 || c->d_latent % 64 || c->d_ff % 64 ||
+      (c->n_shared > 0 && c->d_ff_shared % 64))
+    return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared > 3) return MOE_ERR_UNSUPPORTED;
+
+  const int64_t T = c->T, W = c->n_waves, E = c->n_experts, P = c->n_pools, k = c->top_k;
+  const int64_t Tw = ceil_div(T, W);
+  const int64_t cs = c->cap_send_rows ? c->cap_send_rows
+                                      : capacity(c->send_cap_num, c->send_cap_den, Tw, k, P);
+  const int64_t cr = c->cap_recv_rows ? c->cap_recv_rows
+                                      : capacity(c->recv_cap_num, c->recv_cap_den, Tw, k, E);
+  // every index the kernels form stays inside int32
+  if (W * P * cs > kI32Max || W * E * cr > kI32Max || E * W * cr > kI32Max)
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t eb = c->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t L = c->d_latent, F = c->d_ff;
+  const int64_t S = c->n_shared, Fs = c->d_ff_shared;
+
+  p->tokens_per_wave = Tw;
+  p->cap_send = cs;
+  p->cap_recv = cr;
+  p->experts_per_pool = E / P;
+  p->elem_bytes = eb;
+  p->row_bytes = L * eb;
+  p->ids_offset = cs * L * eb;
+  p->pool_block_bytes = align256(p->ids_offset + cs * 4);
+  p->pools_bytes = W * P * p->pool_block_bytes;
+  p->expert_out_bytes = align256(W * P * cs * L * eb);
+  p->max_expert_rows = W * cr;
+
+  Carver d{nullptr, 0};
+  d.take(W * 3 * 8);  // per-wave counters
+  p->dispatch_ws_bytes = d.used;
+
+  Carver x{nullptr, 0};
+  x.take(E * W * cr * 4);       // expert row lists
+  x.take(E * 4);                // rows per expert
+  x.take(E * W * cr * F * eb);  // SwiGLU hidden rows
+  p->experts_ws_bytes = x.used;
+
+  Carver f{nullptr, 0};
+  f.take(T * L * eb);         // z
+  f.take(T * E * 4);          // logits
+  f.take(T * k * 4);          // topk
+  f.take(T * k * 4);          // gates
+  f.take(T * k * 4);          // pool_slot
+  f.take(T * k * 4);          // recv_slot
+  f.take(W * P * 4);          // pool_count
+  f.take(W * E * 4);          // expert_count
+  f.take(W * E * cr * 4);     // bank_rows
+  f.take(p->pools_bytes);     // pools
+  f.take(p->expert_out_bytes);
+  f.take(T * L * eb);         // y_latent
+  f.take(T * S * Fs * eb);    // shared hidden
+  f.take(3 * 8);              // counters
+  f.take(p->dispatch_ws_bytes);
+  f.take(p->experts_ws_bytes);
+  p->forward_ws_bytes = f.used;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe::DispatchArgs dispatch_args(const moe_config* c, const moe_plan& p, const int32_t* topk,
+                                void* pools, int32_t* pool_slot, int32_t* recv_slot,
+                                int32_t* pool_count, int64_t* wave_counts, int64_t* counts) {
+  moe::DispatchArgs a{};
+  a.topk = topk;
+  a.T = c->T;
+  a.k = c->top_k;
+  a.E = c->n_experts;
+  a.P = c->n_pools;
+  a.W = c->n_waves;
+  a.Tw = p.tokens_per_wave;
+  a.cap_send = p.cap_send;
+  a.cap_recv = p.cap_recv;
+  a.pool_slot = pool_slot;
+  a.recv_slot = recv_slot;
+  a.pool_count = pool_count;
+  a.pools = static_cast<char*>(pools);
+  a.block_bytes = p.pool_block_bytes;
+  a.ids_offset = p.ids_offset;
+  a.row_bytes = p.row_bytes;
+  a.wave_counts = wave_counts;
+  a.counts = counts;
+  return a;
+}
+
+moe_status run_dispatch(const moe_config* c, const moe_plan& p, const int32_t* topk, const void* z,
+                        void* pools, int32_t* pool_slot, int32_t* recv_slot, int32_t* bank_rows,
+                        int32_t* pool_count, int32_t* expert_count, int64_t* counts, void* ws,
+                        hipStream_t s, Marks* m) {
+  Carver cv{static_cast<char*>(ws), 0};
+  int64_t* wave_counts = static_cast<int64_t*>(cv.take(c->n_waves * 3 * 8));
+  const moe::DispatchArgs a =
+      dispatch_args(c, p, topk, pools, pool_slot, recv_slot, pool_count, wave_counts, counts);
+  hipError_t e = moe::launch_assign(a, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e == hipSuccess) e = moe::launch_scatter_rows(a, z, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e == hipSuccess) e = moe::launch_recv_bin(a, bank_rows, expert_count, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  return hip_status(e);
+}
+
+moe_status run_experts(const moe_config* c, const moe_plan& p, const void* pools,
+                       const int32_t* bank_rows, const int32_t* expert_count, const void* wg,
+                       const void* wu, const void* wd, void* expert_out, void* ws,
+                       hipStream_t s, Marks* m) {
+  const int E = c->n_experts;
+  const int max_rows = (int)p.max_expert_rows;
+  Carver cv{static_cast<char*>(ws), 0};
+  int32_t* erow = static_cast<int32_t*>(cv.take((int64_t)E * max_rows * 4));
+  int32_t* rows_total = static_cast<int32_t*>(cv.take((int64_t)E * 4));
+  void* H = cv.take((int64_t)E * max_rows * c->d_ff * p.elem_bytes);
+  hipError_t e = moe::launch_expert_rows(bank_rows, expert_count, E, c->n_pools, c->n_waves,
+                                         p.cap_send, p.cap_recv, erow, rows_total, max_rows, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::ExpertGateUp gu{};
+  gu.pools = static_cast<const char*>(pools);
+  gu.block_bytes = p.pool_block_bytes;
+  gu.row_bytes = p.row_bytes;
+  gu.cap_send = (int)p.cap_send;
+  gu.erow = erow;
+  gu.rows_total = rows_total;
+  gu.E = E;
+  gu.max_rows = max_rows;
+  gu.F = c->d_ff;
+  gu.L = c->d_latent;
+  gu.Wg = wg;
+  gu.Wu = wu;
+  gu.H = H;
+  e = moe::launch_expert_gate_up(c->dtype, gu, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::ExpertDown dn{};
+  dn.H = H;
+  dn.erow = erow;
+  dn.rows_total = rows_total;
+  dn.E = E;
+  dn.max_rows = max_rows;
+  dn.F = c->d_ff;
+  dn.L = c->d_latent;
+  dn.Wd = wd;
+  dn.out = expert_out;
+  e = moe::launch_expert_down(c->dtype, dn, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  return hip_status(e);
+}
+
+moe_status run_combine(const moe_config* c, const moe_plan& p, const void* expert_out,
+                       const int32_t* topk, const int32_t* pool_slot, const int32_t* recv_slot,
+                       const float* gates, void* y_latent, hipStream_t s) {
+  moe::CombineArgs a{};
+  a.expert_out = static_cast<const char*>(expert_out);
+  a.topk = topk;
+  a.pool_slot = pool_slot;
+  a.recv_slot = recv_slot;
+  a.gates = gates;
+  a.T = c->T;
+  a.Tw = p.tokens_per_wave;
+  a.k = c->top_k;
+  a.E = c->n_experts;
+  a.P = c->n_pools;
+  a.cap_send = p.cap_send;
+  a.row_bytes = p.row_bytes;
+  a.y = y_latent;
+  return hip_status(moe::launch_combine(c->dtype, a, s));
+}
+
+}  // namespace
+
+MOE_API const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported shape";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small or misaligned";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+  }
+  return "unknown moe_status";
+}
+
+MOE_API int32_t moe_version(void) { return 100; }
+
+MOE_API moe_status moe_make_plan(const moe_config* cfg, moe_plan* plan) {
+  return plan_impl(cfg, plan);
+}
+
+MOE_API moe_status moe_route(const moe_config* cfg, const float* logits, const float* bias,
+                             int32_t* topk_idx, float* gates, void* stream) {
+  moe_status st = check_route_shape(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->top_k > cfg->n_experts) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!logits || !topk_idx || !gates)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_topk_gates(logits, bias, cfg->T, cfg->n_experts, cfg->top_k,
+                                           topk_idx, gates, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const void* z,
+                                void* pools, int32_t* pool_slot, int32_t* recv_slot,
+                                int32_t* bank_rows, int32_t* pool_count, int32_t* expert_count,
+                                int64_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  moe_plan p;
+  moe_status st = plan_impl(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!pool_count || !expert_count || !counts) return MOE_ERR_INVALID_ARG;
+  if ((p.pools_bytes > 0 && !pools) || (p.cap_recv > 0 && !bank_rows)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!topk_idx || !z || !pool_slot || !recv_slot)) return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.dispatch_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+  return run_dispatch(cfg, p, topk_idx, z, pools, pool_slot, recv_slot, bank_rows, pool_count,
+                      expert_count, counts, ws, static_cast<hipStream_t>(stream), nullptr);
+}
+
+MOE_API moe_status moe_experts(const moe_config* cfg, const void* pools, const int32_t* bank_rows,
+                               const int32_t* expert_count, const void* w_gate, const void* w_up,
+                               const void* w_down, void* expert_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  moe_plan p;
+  moe_status st = plan_impl(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!expert_count || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARG;
+  if ((p.pools_bytes > 0 && (!pools || !expert_out)) || (p.cap_recv > 0 && !bank_rows))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.experts_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+  return run_experts(cfg, p, pools, bank_rows, expert_count, w_gate, w_up, w_down, expert_out, ws,
+                     static_cast<hipStream_t>(stream), nullptr);
+}
+
+MOE_API moe_status moe_combine(const moe_config* cfg, const void* expert_out,
+                               const int32_t* topk_idx, const int32_t* pool_slot,
+                               const int32_t* recv_slot, const float* gates, void* y_latent,
+                               void* stream) {
+  moe_plan p;
+  moe_status st = plan_impl(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!expert_out || !topk_idx || !pool_slot || !recv_slot || !gates || !y_latent))
+    return MOE_ERR_INVALID_ARG;
+  return run_combine(cfg, p, expert_out, topk_idx, pool_slot, recv_slot, gates, y_latent,
+                     static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                        const moe_taps* taps, int64_t* counts, void* ws, size_t ws_bytes,
+                        void* stream, void* const* events, int n_events) {
+  moe_plan p;
+  moe_status st = plan_impl(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->top_k > cfg->n_experts) return MOE_ERR_INVALID_ARG;
+  // the router GEMM writes fp32 logit rows in 16-byte chunks
+  if (cfg->n_experts % 4) return MOE_ERR_UNSUPPORTED;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (!w->w_latent || !w->w_router || !w->w_gate || !w->w_up || !w->w_down || !w->w_up_proj)
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.forward_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+
+  const moe_taps none{};
+  const moe_taps& tp = taps ? *taps : none;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = cfg->T, W = cfg->n_waves, E = cfg->n_experts, P = cfg->n_pools,
+                k = cfg->top_k;
+  const int64_t L = cfg->d_latent, D = cfg->d_model, S = cfg->n_shared, Fs = cfg->d_ff_shared;
+  const int64_t eb = p.elem_bytes;
+  const int dt = cfg->dtype;
+
+  Carver cv{static_cast<char*>(ws), 0};
+  auto pick = [&](void* tap, int64_t bytes) {
+    void* q = cv.take(bytes);
+    return tap ? tap : q;
+  };
+  void* z = pick(tp.z, T * L * eb);
+  float* logits = static_cast<float*>(pick(tp.logits, T * E * 4));
+  int32_t* topk = static_cast<int32_t*>(pick(tp.topk_idx, T * k * 4));
+  float* gates = static_cast<float*>(pick(tp.gates, T * k * 4));
+  int32_t* pool_slot = static_cast<int32_t*>(pick(tp.pool_slot, T * k * 4));
+  int32_t* recv_slot = static_cast<int32_t*>(pick(tp.recv_slot, T * k * 4));
+  int32_t* pool_count = static_cast<int32_t*>(pick(tp.pool_count, W * P * 4));
+  int32_t* expert_count = static_cast<int32_t*>(pick(tp.expert_count, W * E * 4));
+  int32_t* bank_rows = static_cast<int32_t*>(pick(tp.bank_rows, W * E * p.cap_recv * 4));
+  void* pools = pick(tp.pools, p.pools_bytes);
+  void* expert_out = pick(tp.expert_out, p.expert_out_bytes);
+  void* y_lat = pick(tp.y_latent, T * L * eb);
+  void* hs = cv.take(T * S * Fs * eb);
+  int64_t* cnt = static_cast<int64_t*>(pick(counts, 3 * 8));
+  void* dws = cv.take(p.dispatch_ws_bytes);
+  void* xws = cv.take(p.experts_ws_bytes);
+
+  Marks mk{events, n_events, 0};
+  Marks* m = &mk;
+  hipError_t e = m->mark(s);  // start of stage 0
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // latent projection z = x W_lat^T
+  moe::GemmDense g{};
+  g.nseg = 1;
+  g.seg[0] = {x, D, w->w_latent, D, (int)D};
+  g.C = z;
+  g.ldc = L;
+  g.M = (int)T;
+  g.N = (int)L;
+  e = moe::launch_gemm_dense(dt, dt, g, s);
+  if (e == hipSuccess) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // router logits (fp32) = z W_r^T
+  g.seg[0] = {z, L, w->w_router, L, (int)L};
+  g.C = logits;
+  g.ldc = E;
+  g.N = (int)E;
+  e = moe::launch_gemm_dense(dt, moe::DT_F32, g, s);
+  if (e == hipSuccess) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_topk_gates(logits, w->router_bias, T, (int)E, (int)k, topk, gates, s);
+  if (e == hipSuccess) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  st = run_dispatch(cfg, p, topk, z, pools, pool_slot, recv_slot, bank_rows, pool_count,
+                    expert_count, cnt, dws, s, m);
+  if (st != MOE_OK) return st;
+  st = run_experts(cfg, p, pools, bank_rows, expert_count, w->w_gate, w->w_up, w->w_down,
+                   expert_out, xws, s, m);
+  if (st != MOE_OK) return st;
+  st = run_combine(cfg, p, expert_out, topk, pool_slot, recv_slot, gates, y_lat, s);
+  if (st == MOE_OK && m->mark(s) != hipSuccess) st = MOE_ERR_HIP;
+  if (st != MOE_OK) return st;
+  // shared experts' hidden rows: silu(x Wg_s^T) * (x Wu_s^T), [T][S*Fs]
+  if (S > 0) {
+    e = moe::launch_swiglu_dense(dt, x, D, w->ws_gate, w->ws_up, (int)S, (int)Fs, (int)D, (int)T,
+                                 hs, S * Fs, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (m->mark(s) != hipSuccess) return MOE_ERR_HIP;
+  // y = y_lat W_up^T + sum_s hs_s Wd_s^T: one accumulation over K segments
+  moe::GemmDense o{};
+  o.nseg = 1 + (int)S;
+  o.seg[0] = {y_lat, L, w->w_up_proj, L, (int)L};
+  for (int sh = 0; sh < S; ++sh)
+    o.seg[1 + sh] = {static_cast<const char*>(hs) + sh * Fs * eb, S * Fs,
+                     static_cast<const char*>(w->ws_down) + sh * D * Fs * eb, Fs, (int)Fs};
+  o.C = y;
+  o.ldc = D;
+  o.M = (int)T;
+  o.N = (int)D;
+  e = moe::launch_gemm_dense(dt, dt, o, s);
+  if (e == hipSuccess) e = m->mark(s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+MOE_API moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                               const moe_taps* taps, int64_t* counts, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return forward_impl(cfg, w, x, y, taps, counts, ws, ws_bytes, stream, nullptr, 0);
+}
+
+MOE_API moe_status moe_forward_profiled(const moe_config* cfg, const moe_weights* w, const void* x,
+                                        void* y, const moe_taps* taps, int64_t* counts, void* ws,
+                                        size_t ws_bytes, void* stream, void* const* stage_events,
+                                        int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && !stage_events)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, w, x, y, taps, counts, ws, ws_bytes, stream, stage_events, n_events);
+}
+
+MOE_API int32_t moe_forward_stage_count(void) { return kStages; }

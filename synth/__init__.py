@@ -258,3 +258,59 @@ def make_recv_share(seed: int = 0, device="cpu", T: Optional[int] = None,
     return dict(T=T, k=k, W=W, Tw=Tw, n_local=n_local, L=L, F=F, cap_wave=cw,
                 rows=rows, counts=counts, expert_of=expert_of, slot_of=slot_of,
                 gates=gates, **wts)
+
+
+# --------------------------------------------------------------------------
+# inputs of single-step cases
+# --------------------------------------------------------------------------
+
+_CASE = dict(logits=20, topk=21, rows=22, gates=23, bias=24)
+
+
+def logits_case(T: int, E: int, seed: int, kind: str = "normal") -> torch.Tensor:
+    """fp32 router logits [T, E] (CPU).
+
+    normal: N(0, 1).  ties: multiples of 0.5 in [-1.5, 1.0] with signed zeros,
+    so equal scores are common.  tiny: N(0, 1) * 2^-20 plus 1.0, so scores
+    differ in the last bits of fp32.
+    """
+    g = _gen("cpu", seed, _CASE["logits"], T * 4096 + E)
+    if kind == "normal":
+        return torch.randn((T, E), generator=g, dtype=torch.float32)
+    if kind == "ties":
+        v = torch.randint(-3, 3, (T, E), generator=g).to(torch.float32) * 0.5
+        neg = torch.rand((T, E), generator=g) < 0.5
+        return torch.where((v == 0) & neg, torch.full_like(v, -0.0), v)
+    if kind == "tiny":
+        return 1.0 + torch.randn((T, E), generator=g, dtype=torch.float32) * 2.0 ** -20
+    raise ValueError(kind)
+
+
+def bias_case(E: int, seed: int, std: float) -> torch.Tensor:
+    g = _gen("cpu", seed, _CASE["bias"], E)
+    return torch.randn(E, generator=g, dtype=torch.float32) * std
+
+
+def topk_case(T: int, E: int, k: int, seed: int, skew: float = 0.0) -> torch.Tensor:
+    """int32 [T, k]: k distinct experts per token, drawn without replacement
+    with probabilities proportional to exp(-skew * rank(e)) for a seeded
+    popularity order (Gumbel-top-k sampling)."""
+    g = _gen("cpu", seed, _CASE["topk"], T * 4096 + E * 64 + k)
+    order = torch.randperm(E, generator=g)
+    logp = torch.empty(E, dtype=torch.float64)
+    logp[order] = -skew * torch.arange(E, dtype=torch.float64)
+    u = torch.rand((T, E), generator=g, dtype=torch.float64).clamp_min(1e-300)
+    keys = logp[None, :] - torch.log(-torch.log(u))
+    return torch.topk(keys, k, dim=1).indices.to(torch.int32)
+
+
+def rows_case(n: int, L: int, seed: int, dtype: str, sub: int = 0) -> torch.Tensor:
+    """[n, L] N(0, 1) rows (CPU), e.g. activations or expert outputs."""
+    return normal((n, L), seed, _CASE["rows"], "cpu", 1.0, dtype, sub=sub)
+
+
+def gates_case(T: int, k: int, seed: int) -> torch.Tensor:
+    """fp32 [T, k] positive weights summing to one (Dirichlet(1))."""
+    g = _gen("cpu", seed, _CASE["gates"], T * 64 + k)
+    spac = -torch.log1p(-torch.rand((T, k), generator=g, dtype=torch.float64))
+    return (spac / spac.sum(dim=1, keepdim=True)).to(torch.float32)

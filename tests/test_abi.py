@@ -1,0 +1,169 @@
+"""The C-ABI library loads, exports what include/moe.h declares, and its
+host-side plan and validation behave (no GPU work: every call here returns
+before anything is enqueued)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import synth
+import routing_capacity_dispatch_amd as rcd
+from routing_capacity_dispatch_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(abi.LIB_PATH):
+        pytest.fail("libmoe.so is not built (python -m routing_capacity_dispatch_amd.build)")
+    return abi.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["moe_make_plan", "moe_route", "moe_dispatch", "moe_experts", "moe_combine",
+              "moe_forward", "moe_status_string"]:
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    # the binding's signature table covers exactly the declared functions
+    assert sorted(abi.SIGNATURES) == declared_functions()
+
+
+def test_struct_layouts_match_header():
+    # sizes implied by the header's field lists (natural alignment, no packing)
+    assert C.sizeof(abi.MoeConfig) == 8 + 13 * 4 + 4 + 2 * 8 + 2 * 4
+    assert C.sizeof(abi.MoePlan) == 14 * 8
+    assert C.sizeof(abi.MoeWeights) == 10 * 8
+    assert C.sizeof(abi.MoeTaps) == 12 * 8
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_string(s).decode().startswith(abi.STATUS_NAMES[s])
+    assert lib.moe_version() >= 100
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "mid_bf16", "marin_16k", "zipf_64k"])
+def test_plan_matches_oracle_capacity(lib, name):
+    w = synth.workload(name)
+    p = rcd.plan(rcd.config_of(w))
+    o = oracle.capacity_plan(w.T, w.top_k, w.n_experts, w.n_pools, w.n_waves)
+    assert (p["tokens_per_wave"], p["cap_send"], p["cap_recv"]) == (o["Tw"], o["cap_send"], o["cap_recv"])
+    eb = 2 if w.dtype == "bf16" else 4
+    assert p["row_bytes"] == w.d_latent * eb
+    assert p["pool_block_bytes"] % 256 == 0
+    assert p["pool_block_bytes"] >= p["cap_send"] * (w.d_latent * eb + 4)
+    assert p["pools_bytes"] == w.n_waves * w.n_pools * p["pool_block_bytes"]
+    assert p["max_expert_rows"] == w.n_waves * p["cap_recv"]
+    for k in ("dispatch_ws_bytes", "experts_ws_bytes", "forward_ws_bytes"):
+        assert p[k] % 256 == 0 and p[k] > 0
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 5, 86, 100, 4095, 65536])
+@pytest.mark.parametrize("k,E,P,W", [(1, 4, 1, 1), (2, 16, 4, 3), (8, 384, 64, 3), (8, 384, 384, 2),
+                                     (3, 12, 3, 5)])
+def test_plan_capacity_sweep(lib, T, k, E, P, W):
+    cfg = rcd.make_config(T, 64, 64, E, P, k, 64, n_waves=W, dtype="bf16")
+    p = rcd.plan(cfg)
+    o = oracle.capacity_plan(T, k, E, P, W)
+    assert (p["tokens_per_wave"], p["cap_send"], p["cap_recv"]) == (o["Tw"], o["cap_send"], o["cap_recv"])
+
+
+def test_recv_share_plan(lib):
+    sh = synth.RECV_SHARE
+    cfg = rcd.make_config(sh["T"], 64, sh["d_latent"], sh["n_local"], 1, sh["top_k"], sh["d_ff"],
+                          n_waves=3, cap_send_rows=sh["n_local"] * sh["cap_wave"],
+                          cap_recv_rows=sh["cap_wave"])
+    p = rcd.plan(cfg)
+    assert p["cap_recv"] == 33497 and p["cap_send"] == 6 * 33497
+    assert p["max_expert_rows"] == 3 * 33497
+
+
+def _status(fn):
+    try:
+        fn()
+    except abi.MoeError as e:
+        return e.status
+    return abi.MOE_OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_pools", 5, abi.MOE_ERR_INVALID_ARG),        # 16 % 5 != 0
+    ("top_k", 65, abi.MOE_ERR_UNSUPPORTED),         # k > 64
+    ("top_k", 0, abi.MOE_ERR_INVALID_ARG),
+    ("n_waves", 0, abi.MOE_ERR_INVALID_ARG),
+    ("T", -1, abi.MOE_ERR_INVALID_ARG),
+    ("d_model", 0, abi.MOE_ERR_INVALID_ARG),
+    ("send_cap_den", 0, abi.MOE_ERR_INVALID_ARG),
+    ("recv_cap_num", -1, abi.MOE_ERR_INVALID_ARG),
+    ("dtype", 7, abi.MOE_ERR_INVALID_ARG),
+    ("reserved", 1, abi.MOE_ERR_INVALID_ARG),
+    ("d_latent", 100, abi.MOE_ERR_UNSUPPORTED),     # not a multiple of 64
+    ("d_ff", 96, abi.MOE_ERR_UNSUPPORTED),
+    ("n_shared", 4, abi.MOE_ERR_UNSUPPORTED),
+])
+def test_plan_rejects(lib, field, value, status):
+    cfg = rcd.config_of(synth.workload("tiny_fp32"))
+    setattr(cfg, field, value)
+    assert _status(lambda: rcd.plan(cfg)) == status
+
+
+def test_too_many_experts_unsupported(lib):
+    cfg = rcd.make_config(16, 64, 64, 2048, 1, 2, 64)
+    assert _status(lambda: rcd.plan(cfg)) == abi.MOE_ERR_UNSUPPORTED
+
+
+def test_calls_validate_before_enqueue(lib):
+    cfg = rcd.config_of(synth.workload("tiny_fp32"))
+    nul = None
+    # null data pointers
+    assert lib.moe_route(C.byref(cfg), nul, nul, nul, nul, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(C.byref(cfg), nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, 0,
+                            nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(C.byref(cfg), nul, nul, nul, nul, nul, nul, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_experts(C.byref(cfg), nul, nul, nul, nul, nul, nul, nul, nul, 0,
+                           nul) == abi.MOE_ERR_INVALID_ARG
+    w = abi.MoeWeights()
+    assert lib.moe_forward(C.byref(cfg), C.byref(w), nul, nul, nul, nul, nul, 0,
+                           nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(C.byref(cfg), nul, nul, nul, nul, nul, nul, 0,
+                           nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_make_plan(nul, nul) == abi.MOE_ERR_INVALID_ARG
+    # short or misaligned workspace (fake, never dereferenced: rejected first)
+    fake = C.c_void_p(0x100000)
+    p = rcd.plan(cfg)
+    assert lib.moe_dispatch(C.byref(cfg), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                            fake, p["dispatch_ws_bytes"] - 1, nul) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_dispatch(C.byref(cfg), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                            C.c_void_p(0x100010), p["dispatch_ws_bytes"], nul) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_experts(C.byref(cfg), fake, fake, fake, fake, fake, fake, fake, fake,
+                           p["experts_ws_bytes"] - 256, nul) == abi.MOE_ERR_WORKSPACE
+    ww = abi.MoeWeights(*([0x100000] * 10))
+    assert lib.moe_forward(C.byref(cfg), C.byref(ww), fake, fake, nul, nul, fake,
+                           p["forward_ws_bytes"] - 1, nul) == abi.MOE_ERR_WORKSPACE
+    # bad shapes on the route call
+    bad = rcd.config_of(synth.workload("tiny_fp32"))
+    bad.top_k = 20   # > E = 16
+    assert lib.moe_route(C.byref(bad), fake, nul, fake, fake, nul) == abi.MOE_ERR_INVALID_ARG
+    bad.top_k = 2
+    bad.n_experts = 4096
+    assert lib.moe_route(C.byref(bad), fake, nul, fake, fake, nul) == abi.MOE_ERR_UNSUPPORTED
