@@ -35,6 +35,8 @@ COMMON = [
     # gfx950: keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-parameter",
+    # gemm_core.h sets M0 in inline assembly for its global -> LDS loads
+    "-Wno-inline-asm",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

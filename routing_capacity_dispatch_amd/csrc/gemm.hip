@@ -1,4 +1,6 @@
-// MFMA GEMMs of the MoE branch for gfx950.
+// MFMA GEMMs of the MoE branch for gfx950: the fp32 paths and the router
+// GEMM (bf16 in, fp32 logits out).  bf16 -> bf16 contractions go to the
+// gfx950 core in gemm_bf16.hip.
 //
 // Every contraction here is C = A * B^T with both operands contiguous along
 // K (weights are stored [out, in]).  One workgroup of 4 wavefronts computes a
@@ -329,10 +331,9 @@ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 hipError_t launch_gemm_dense(int in_dt, int out_dt, const GemmDense& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (in_dt == DT_BF16 && out_dt == DT_BF16) return launch_gemm_dense_bf16(g, s);
   const dim3 grid(cdiv(g.N, BN), cdiv(g.M, BM));
-  if (in_dt == DT_BF16 && out_dt == DT_BF16)
-    gemm_dense_kernel<bf16_t, bf16_t><<<grid, NTHR, 0, s>>>(g);
-  else if (in_dt == DT_BF16 && out_dt == DT_F32)
+  if (in_dt == DT_BF16 && out_dt == DT_F32)
     gemm_dense_kernel<bf16_t, float><<<grid, NTHR, 0, s>>>(g);
   else if (in_dt == DT_F32 && out_dt == DT_F32)
     gemm_dense_kernel<float, float><<<grid, NTHR, 0, s>>>(g);
@@ -345,7 +346,8 @@ hipError_t launch_swiglu_dense(int dt, const void* A, int64_t lda, const void* W
                                const void* Wu, int G, int F, int K, int M, void* C,
                                int64_t ldc, hipStream_t s) {
   if (M <= 0 || G <= 0) return hipSuccess;
-  const int eb = dt == DT_BF16 ? 2 : 4;
+  if (dt == DT_BF16) return launch_swiglu_dense_bf16(A, lda, Wg, Wu, G, F, K, M, C, ldc, s);
+  const int eb = 4;
   SwigluArgs p{};
   p.A = static_cast<const char*>(A);
   p.lda_bytes = lda * eb;
@@ -357,15 +359,13 @@ hipError_t launch_swiglu_dense(int dt, const void* A, int64_t lda, const void* W
   p.C = static_cast<char*>(C);
   p.ldc_bytes = ldc * eb;
   const dim3 grid(F / 64, cdiv(M, BM), G);
-  if (dt == DT_BF16)
-    swiglu_kernel<bf16_t, false><<<grid, NTHR, 0, s>>>(p);
-  else
-    swiglu_kernel<float, false><<<grid, NTHR, 0, s>>>(p);
+  swiglu_kernel<float, false><<<grid, NTHR, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_gate_up(int dt, const ExpertGateUp& a, hipStream_t s) {
   if (a.E <= 0 || a.max_rows <= 0) return hipSuccess;
+  if (dt == DT_BF16) return launch_expert_gate_up_bf16(a, s);
   SwigluArgs p{};
   p.pools = a.pools;
   p.block_bytes = a.block_bytes;
@@ -380,20 +380,15 @@ hipError_t launch_expert_gate_up(int dt, const ExpertGateUp& a, hipStream_t s) {
   p.K = a.L;
   p.C = static_cast<char*>(a.H);
   const dim3 grid(a.F / 64, cdiv(a.max_rows, BM), a.E);
-  if (dt == DT_BF16)
-    swiglu_kernel<bf16_t, true><<<grid, NTHR, 0, s>>>(p);
-  else
-    swiglu_kernel<float, true><<<grid, NTHR, 0, s>>>(p);
+  swiglu_kernel<float, true><<<grid, NTHR, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_down(int dt, const ExpertDown& a, hipStream_t s) {
   if (a.E <= 0 || a.max_rows <= 0) return hipSuccess;
+  if (dt == DT_BF16) return launch_expert_down_bf16(a, s);
   const dim3 grid(cdiv(a.L, BN), cdiv(a.max_rows, BM), a.E);
-  if (dt == DT_BF16)
-    expert_down_kernel<bf16_t><<<grid, NTHR, 0, s>>>(a);
-  else
-    expert_down_kernel<float><<<grid, NTHR, 0, s>>>(a);
+  expert_down_kernel<float><<<grid, NTHR, 0, s>>>(a);
   return hipGetLastError();
 }
 

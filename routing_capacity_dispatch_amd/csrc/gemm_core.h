@@ -1,0 +1,205 @@
+// bf16 MFMA GEMM core for gfx950: C = A * B^T, A [M][K] and B [N][K] both
+// contiguous along K (weights are stored [out, in]).
+//
+// Tile BM x BN per workgroup of WGM x WGN wavefronts, each wavefront owning a
+// (BM/WGM) x (BN/WGN) sub-tile as 16x16 blocks of v_mfma_f32_16x16x32_bf16.
+// Eight wavefronts (two per SIMD) keep the matrix cores busy while the other
+// wavefront of the SIMD waits on LDS.  K advances in tiles of 64 bf16 (128
+// bytes per tile row).  Operand tiles go straight from global memory into
+// LDS with global_load_lds_dwordx4 (no VGPR round trip): one instruction
+// moves 8 tile rows (1 KiB), lane l writing the 16 bytes at LDS offset 16 l.
+// Rows keep an XOR swizzle of their 16-byte chunks (physical chunk = logical
+// chunk ^ (row & 7)), so lane l of an instruction loads logical chunk
+// (l & 7) ^ (l >> 3) of row l >> 3, and the fragment reads (16 rows, one
+// chunk each) hit 8 distinct chunk positions.  Two LDS stages: the loads of
+// tile k+1 are in flight while tile k feeds the MFMAs.
+//
+// Row sources are per-lane pointers, so the same mainloop serves dense
+// operands, rows gathered through an index list and interleaved gate/up
+// weight rows.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace core {
+
+#define MOE_LDS __attribute__((address_space(3)))
+
+// BK_: bf16 of K per tile (32 or 64: tile rows of 64 or 128 bytes);
+// NS_: LDS stages (NS - 1 tiles in flight while one feeds the MFMAs).
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, NS = NS_;
+  static constexpr int RB = BK * 2;                    // bytes per tile row
+  static constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;                // rows per load instruction
+  static constexpr int KS = BK / 32;                   // MFMA K sub-steps per tile
+  static constexpr int NW = WGM * WGN;                 // wavefronts
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;   // wavefront sub-tile
+  static constexpr int MI = WM / 16, NI = WN / 16;     // 16x16 blocks per wavefront
+  static constexpr int A_INS = BM / (RPI * NW);        // load instructions per wavefront per K tile
+  static constexpr int B_INS = BN / (RPI * NW);
+  static constexpr int A_BYTES = BM * RB;
+  static constexpr int B_BYTES = BN * RB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int MAIN_LDS = NS * STAGE;
+  static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows come in whole loads per wavefront");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wavefront sub-tiles are whole 16x16 blocks");
+  // chunk swizzle of row r: XOR applied to the 16-byte chunk index, chosen so
+  // that 8 consecutive rows read at one logical chunk hit 8 distinct 16-byte
+  // positions of a 128-byte bank line
+  __device__ __forceinline__ static int swz(int r) { return RB == 128 ? (r & 7) : ((r >> 1) & 3); }
+};
+
+// Tile row that lane `lane` of wavefront `wave` loads with instruction i.
+template <class TL>
+__device__ __forceinline__ int load_row(int i, int wave, int lane) {
+  return (i * TL::NW + wave) * TL::RPI + lane / TL::CPR;
+}
+// Byte offset inside that row: the logical chunk whose physical position is
+// this lane's slot (instruction base rows are multiples of RPI, so the row's
+// swizzle depends on the lane only).
+template <class TL>
+__device__ __forceinline__ int load_col(int lane) {
+  return ((lane % TL::CPR) ^ TL::swz(lane / TL::CPR)) << 4;
+}
+
+// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes land at
+// lds_wave_base + 16 l.  Written as inline assembly so the compiler does not
+// make every later LDS read wait for it; the mainloop waits explicitly
+// (s_waitcnt vmcnt(0) + barrier) before reading a stage.
+__device__ __forceinline__ void lds_load16(const char* g, char* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MOE_LDS char*)lds_wave_base)));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g) : "memory", "m0");
+}
+
+template <class TL>
+struct Acc {
+  f32x4_t v[TL::MI][TL::NI];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::NI; ++j) v[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Issue the loads of one K tile into one stage.  a_src / b_src: per-lane row
+// pointers (already offset by load_col), advanced by `koff` bytes.
+template <class TL>
+__device__ __forceinline__ void issue_tile(const char* const (&a_src)[TL::A_INS],
+                                           const char* const (&b_src)[TL::B_INS], int64_t koff,
+                                           char* stage, int wave) {
+#pragma unroll
+  for (int i = 0; i < TL::A_INS; ++i) lds_load16(a_src[i] + koff, stage + (i * TL::NW + wave) * 1024);
+#pragma unroll
+  for (int i = 0; i < TL::B_INS; ++i)
+    lds_load16(b_src[i] + koff, stage + TL::A_BYTES + (i * TL::NW + wave) * 1024);
+}
+
+// MFMAs of one staged K tile: fragments of K sub-step 0 are read first; the
+// reads of sub-step 1 (64-wide K tiles) are interleaved with the MFMAs of
+// sub-step 0.
+template <class TL>
+__device__ __forceinline__ void compute_tile(const char* stage, Acc<TL>& acc, int wm, int wn, int lane) {
+  const char* a = stage + (wm * TL::WM + (lane & 15)) * TL::RB;
+  const char* b = stage + TL::A_BYTES + (wn * TL::WN + (lane & 15)) * TL::RB;
+  const int sw = TL::swz(lane & 15);
+  uint4 fa[TL::KS][TL::MI], fb[TL::KS][TL::NI];
+#pragma unroll
+  for (int ks = 0; ks < TL::KS; ++ks) {
+    const int off = ((ks * 4 + (lane >> 4)) ^ sw) << 4;
+#pragma unroll
+    for (int mi = 0; mi < TL::MI; ++mi) fa[ks][mi] = ld16(a + mi * 16 * TL::RB + off);
+#pragma unroll
+    for (int ni = 0; ni < TL::NI; ++ni) fb[ks][ni] = ld16(b + ni * 16 * TL::RB + off);
+  }
+#pragma unroll
+  for (int ks = 0; ks < TL::KS; ++ks)
+#pragma unroll
+    for (int mi = 0; mi < TL::MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < TL::NI; ++ni)
+        acc.v[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, fa[ks][mi]), __builtin_bit_cast(bf16x8_t, fb[ks][ni]), acc.v[mi][ni], 0, 0,
+            0);
+  constexpr int NR = TL::MI + TL::NI;
+  constexpr int NM = TL::MI * TL::NI;
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  if (TL::KS == 2) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+}
+
+// Wait until at most n load instructions of this wavefront are in flight,
+// then synchronise the workgroup.
+template <int n>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  if (n == 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Accumulate K range [0, ktiles * BK) into acc.  NS stages in `lds`: tiles
+// kt+1 .. kt+NS-1 are in flight while tile kt is consumed.  Ends with a
+// barrier so the caller may reuse the LDS.
+template <class TL>
+__device__ __forceinline__ void mainloop(const char* const (&a_src)[TL::A_INS],
+                                         const char* const (&b_src)[TL::B_INS], int ktiles, char* lds,
+                                         Acc<TL>& acc) {
+  constexpr int P = TL::A_INS + TL::B_INS;  // load instructions per tile per wavefront
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  if (ktiles <= 0) return;
+#pragma unroll
+  for (int s = 0; s < TL::NS - 1; ++s)
+    if (s < ktiles) issue_tile<TL>(a_src, b_src, (int64_t)s * TL::RB, lds + s * TL::STAGE, wave);
+  int stage = 0;
+  for (int kt = 0; kt < ktiles; ++kt) {
+    // tiles issued after tile kt: min(NS - 2, ktiles - 1 - kt)
+    const int after = min(TL::NS - 2, ktiles - 1 - kt);
+    if (TL::NS >= 4 && after >= 2)
+      wait_loads<2 * P>();
+    else if (TL::NS >= 3 && after >= 1)
+      wait_loads<P>();
+    else
+      wait_loads<0>();
+    const int nxt = kt + TL::NS - 1;
+    if (nxt < ktiles) {
+      int ns = stage + TL::NS - 1;
+      if (ns >= TL::NS) ns -= TL::NS;
+      issue_tile<TL>(a_src, b_src, (int64_t)nxt * TL::RB, lds + ns * TL::STAGE, wave);
+    }
+    compute_tile<TL>(lds + stage * TL::STAGE, acc, wm, wn, lane);
+    if (++stage == TL::NS) stage = 0;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+}
+
+// Tile coordinates of register r of block (mi, ni) for this lane.
+template <class TL>
+__device__ __forceinline__ int acc_row(int wm, int mi, int lane, int r) {
+  return wm * TL::WM + mi * 16 + (lane >> 4) * 4 + r;
+}
+template <class TL>
+__device__ __forceinline__ int acc_col(int wn, int ni, int lane) {
+  return wn * TL::WN + ni * 16 + (lane & 15);
+}
+
+}  // namespace core
+}  // namespace moe

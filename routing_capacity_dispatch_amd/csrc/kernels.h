@@ -65,6 +65,14 @@ struct ExpertDown {
 };
 hipError_t launch_expert_down(int dt, const ExpertDown& a, hipStream_t s);
 
+// bf16 paths on the gfx950 GEMM core (gemm_bf16.hip); the generic launchers
+// above dispatch to them for bf16 inputs and outputs.
+hipError_t launch_gemm_dense_bf16(const GemmDense& g, hipStream_t s);
+hipError_t launch_swiglu_dense_bf16(const void* A, int64_t lda, const void* Wg, const void* Wu, int G,
+                                    int F, int K, int M, void* C, int64_t ldc, hipStream_t s);
+hipError_t launch_expert_gate_up_bf16(const ExpertGateUp& a, hipStream_t s);
+hipError_t launch_expert_down_bf16(const ExpertDown& a, hipStream_t s);
+
 // ---------------------------------------------------------------- routing
 hipError_t launch_topk_gates(const float* logits, const float* bias, int64_t T, int E,
                              int k, int32_t* topk_idx, float* gates, hipStream_t s);
