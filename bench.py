@@ -30,6 +30,69 @@ METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; % bf16 MFMA peak; drop fraction"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 
+# rocprofv3 kernel names of the stages (substrings that all must match)
+STAGE_KERNEL = {
+    "latent": ("dense_bf16_kernel",),
+    "expert_gate_up": ("swiglu_bf16_kernel", "true>"),
+    "expert_down": ("expert_down_bf16_kernel",),
+    "shared_gate_up": ("swiglu_bf16_kernel", "false>"),
+    "output": ("dense_bf16_kernel",),
+    "combine": ("combine_kernel",),
+    "scatter": ("scatter_kernel",),
+}
+COPY_KERNEL = ("copyBuffer",)
+# sources of the GEMM kernels: a measured traffic figure is used only while
+# they are unchanged
+KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "dispatch.hip"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "routing_capacity_dispatch_amd", "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv, write_csv, stage, workload, copy_bytes, out_path, command):
+    """Per-launch HBM bytes of one stage's kernel from two rocprofv3 --pmc
+    counter files (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled
+    by what the same counter reads for a device copy of copy_bytes bytes."""
+    import csv
+
+    def per_dispatch(path, counter, pats):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter or not all(p in r["Kernel_Name"] for p in pats):
+                continue
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return list(vals.values())
+
+    pats = STAGE_KERNEL[stage]
+    f_k = per_dispatch(fetch_csv, "FETCH_SIZE", pats)
+    w_k = per_dispatch(write_csv, "WRITE_SIZE", pats)
+    f_c = per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL)
+    w_c = per_dispatch(write_csv, "WRITE_SIZE", COPY_KERNEL)
+    if not (f_k and w_k and f_c and w_c):
+        raise SystemExit("kernel or copy dispatches missing from the counter files")
+    # the calibration copy is the largest copy dispatch
+    fc, wc = max(f_c), max(w_c)
+    f_scale = copy_bytes / (fc * 1024.0)
+    w_scale = copy_bytes / (wc * 1024.0)
+    fk, wk = sum(f_k) / len(f_k), sum(w_k) / len(w_k)
+    rec = {"workload": workload, "stage": stage, "kernel_pattern": list(pats),
+           "dispatches": [len(f_k), len(w_k)],
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+           "copy_bytes": copy_bytes, "copy_fetch_kib": fc, "copy_write_kib": wc,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale,
+           "source_sha256": kernel_source_hash(), "command": command}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
 
 def stage_work(w, kept, sent):
     """Algorithmic flops (MFMA stages) or bytes (HBM stages) per launch."""
@@ -98,9 +161,24 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="measured HBM bytes per launch of the dominant kernel (JSON)")
+    ap.add_argument("--traffic", default=None,
+                    help="measured HBM bytes per launch of the dominant kernel (JSON; default "
+                         "profiles/traffic_<workload>.json)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one device copy of this many MiB before the warmup (the "
+                         "known-size kernel that scales the PMC byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the dominant kernel's measured traffic from two rocprofv3 "
+                         "--pmc counter files and exit")
+    ap.add_argument("--stage", default="expert_gate_up", help="stage for --summarize-pmc")
+    ap.add_argument("--pmc-command", default="", help="command recorded by --summarize-pmc")
     args = ap.parse_args()
+    if args.traffic is None:
+        args.traffic = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.stage, args.workload,
+                      args.calib_copy_mb * 1024 * 1024, args.traffic, args.pmc_command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -124,6 +202,13 @@ def main():
     x = inp["x"]
     fwd = rcd.Forward(cfg, {k: v for k, v in inp.items() if k != "x"}, dev)
     nst = rcd.stage_count()
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * 1024 * 1024
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     stages = rcd.abi.STAGES
     assert len(stages) == nst
 
@@ -185,9 +270,10 @@ def main():
     if args.traffic and os.path.exists(args.traffic):
         try:
             tr = json.load(open(args.traffic))
-            if tr.get("kernel") == dom and tr.get("workload") == w.name:
-                roof["traffic"] = tr.get("bytes_per_launch")
-        except (OSError, ValueError):
+            if (tr.get("stage") == dom and tr.get("workload") == w.name
+                    and tr.get("source_sha256") == kernel_source_hash()):
+                roof["traffic"] = round(tr["bytes_per_launch"])
+        except (OSError, ValueError, KeyError):
             pass
     gemm_flops = sum(work[s][1] for s in stages if work[s][0] == "mfma")
     gemm_ms = sum(per[s] for s in stages if work[s][0] == "mfma")

@@ -5,7 +5,8 @@
 // Tile shapes: 256 x 256 with 8 wavefronts (64 x 128 each) for the dense
 // contractions, whose M (tokens) and N are large; 192 x 256 with 8
 // wavefronts (96 x 64 each) for the routed experts, whose ~341 rows per
-// expert fit two 192-row tiles with little padding.
+// expert fit two 192-row tiles with little padding.  The experts' weight
+// tiles stream from HBM once each, so they get a third LDS stage.
 //
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
 // every kernel maps its linear block index to a tile such that one XCD gets
@@ -28,7 +29,7 @@ using core::load_row;
 using core::mainloop;
 
 using DenseTile = core::Tile<256, 256, 4, 2, 64, 2>;
-using ExpertTile = core::Tile<192, 256, 2, 4, 64, 2>;
+using ExpertTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;
 
 constexpr int kGroupM = 8;  // M panels per group of the dense tile order
 constexpr int kStagePad = 16;

@@ -11,8 +11,9 @@
 // Rows keep an XOR swizzle of their 16-byte chunks (physical chunk = logical
 // chunk ^ (row & 7)), so lane l of an instruction loads logical chunk
 // (l & 7) ^ (l >> 3) of row l >> 3, and the fragment reads (16 rows, one
-// chunk each) hit 8 distinct chunk positions.  Two LDS stages: the loads of
-// tile k+1 are in flight while tile k feeds the MFMAs.
+// chunk each) hit 8 distinct chunk positions.  NS LDS stages: the loads of
+// the next NS-1 tiles are in flight while one tile feeds the MFMAs (B may
+// take one stage more than A).
 //
 // Row sources are per-lane pointers, so the same mainloop serves dense
 // operands, rows gathered through an index list and interleaved gate/up
@@ -27,10 +28,12 @@ namespace core {
 #define MOE_LDS __attribute__((address_space(3)))
 
 // BK_: bf16 of K per tile (32 or 64: tile rows of 64 or 128 bytes);
-// NS_: LDS stages (NS - 1 tiles in flight while one feeds the MFMAs).
-template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2>
+// NS_: LDS stages of A (NS - 1 tiles in flight while one feeds the MFMAs);
+// NSB_: LDS stages of B, either NS or NS + 1 (B, the weights, then loads one
+// tile further ahead: it is the operand that streams from HBM).
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2, int NSB_ = NS_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, NS = NS_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, NS = NS_, NSB = NSB_;
   static constexpr int RB = BK * 2;                    // bytes per tile row
   static constexpr int CPR = RB / 16;                  // 16-byte chunks per row
   static constexpr int RPI = 1024 / RB;                // rows per load instruction
@@ -43,10 +46,11 @@ struct Tile {
   static constexpr int B_INS = BN / (RPI * NW);
   static constexpr int A_BYTES = BM * RB;
   static constexpr int B_BYTES = BN * RB;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int MAIN_LDS = NS * STAGE;
+  static constexpr int B_BASE = NS * A_BYTES;  // B stages follow the A stages
+  static constexpr int MAIN_LDS = NS * A_BYTES + NSB * B_BYTES;
   static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
-  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert(NS >= 2 && NS <= 5, "2 to 5 stages");
+  static_assert(NSB == NS || (NS == 2 && NSB == 3), "B stages: NS, or 3 with 2 A stages");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows come in whole loads per wavefront");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wavefront sub-tiles are whole 16x16 blocks");
   // chunk swizzle of row r: XOR applied to the 16-byte chunk index, chosen so
@@ -89,26 +93,22 @@ struct Acc {
   }
 };
 
-// Issue the loads of one K tile into one stage.  a_src / b_src: per-lane row
+// Issue the loads of one K tile of A or B into one stage.  src: per-lane row
 // pointers (already offset by load_col), advanced by `koff` bytes.
-template <class TL>
-__device__ __forceinline__ void issue_tile(const char* const (&a_src)[TL::A_INS],
-                                           const char* const (&b_src)[TL::B_INS], int64_t koff,
-                                           char* stage, int wave) {
+template <class TL, int N>
+__device__ __forceinline__ void issue_rows(const char* const (&src)[N], int64_t koff, char* stage, int wave) {
 #pragma unroll
-  for (int i = 0; i < TL::A_INS; ++i) lds_load16(a_src[i] + koff, stage + (i * TL::NW + wave) * 1024);
-#pragma unroll
-  for (int i = 0; i < TL::B_INS; ++i)
-    lds_load16(b_src[i] + koff, stage + TL::A_BYTES + (i * TL::NW + wave) * 1024);
+  for (int i = 0; i < N; ++i) lds_load16(src[i] + koff, stage + (i * TL::NW + wave) * 1024);
 }
 
 // MFMAs of one staged K tile: fragments of K sub-step 0 are read first; the
 // reads of sub-step 1 (64-wide K tiles) are interleaved with the MFMAs of
 // sub-step 0.
 template <class TL>
-__device__ __forceinline__ void compute_tile(const char* stage, Acc<TL>& acc, int wm, int wn, int lane) {
-  const char* a = stage + (wm * TL::WM + (lane & 15)) * TL::RB;
-  const char* b = stage + TL::A_BYTES + (wn * TL::WN + (lane & 15)) * TL::RB;
+__device__ __forceinline__ void compute_tile(const char* sa, const char* sb, Acc<TL>& acc, int wm, int wn,
+                                             int lane) {
+  const char* a = sa + (wm * TL::WM + (lane & 15)) * TL::RB;
+  const char* b = sb + (wn * TL::WN + (lane & 15)) * TL::RB;
   const int sw = TL::swz(lane & 15);
   uint4 fa[TL::KS][TL::MI], fb[TL::KS][TL::NI];
 #pragma unroll
@@ -154,38 +154,78 @@ __device__ __forceinline__ void wait_loads() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Accumulate K range [0, ktiles * BK) into acc.  NS stages in `lds`: tiles
-// kt+1 .. kt+NS-1 are in flight while tile kt is consumed.  Ends with a
-// barrier so the caller may reuse the LDS.
+// Accumulate K range [0, ktiles * BK) into acc.  With NS stages of A and B,
+// tiles kt+1 .. kt+NS-1 are in flight while tile kt is consumed; with 3 B
+// stages and 2 A stages, A(kt+1) and B(kt+1), B(kt+2) are.  Loads return in
+// issue order, so waiting until at most n load instructions of a wavefront
+// are outstanding means all but its last n have landed.  Ends with a barrier
+// so the caller may reuse the LDS.
+//
+// a_kstep / b_kstep: bytes between consecutive K tiles of one row source (the
+// tile row width for row-major operands; a whole packed tile for operands
+// stored tile by tile).
 template <class TL>
 __device__ __forceinline__ void mainloop(const char* const (&a_src)[TL::A_INS],
                                          const char* const (&b_src)[TL::B_INS], int ktiles, char* lds,
-                                         Acc<TL>& acc) {
+                                         Acc<TL>& acc, int64_t a_kstep = TL::RB, int64_t b_kstep = TL::RB) {
   constexpr int P = TL::A_INS + TL::B_INS;  // load instructions per tile per wavefront
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  char* lds_a = lds;
+  char* lds_b = lds + TL::B_BASE;
   if (ktiles <= 0) return;
+  if constexpr (TL::NSB == TL::NS) {
 #pragma unroll
-  for (int s = 0; s < TL::NS - 1; ++s)
-    if (s < ktiles) issue_tile<TL>(a_src, b_src, (int64_t)s * TL::RB, lds + s * TL::STAGE, wave);
-  int stage = 0;
-  for (int kt = 0; kt < ktiles; ++kt) {
-    // tiles issued after tile kt: min(NS - 2, ktiles - 1 - kt)
-    const int after = min(TL::NS - 2, ktiles - 1 - kt);
-    if (TL::NS >= 4 && after >= 2)
-      wait_loads<2 * P>();
-    else if (TL::NS >= 3 && after >= 1)
-      wait_loads<P>();
-    else
-      wait_loads<0>();
-    const int nxt = kt + TL::NS - 1;
-    if (nxt < ktiles) {
-      int ns = stage + TL::NS - 1;
-      if (ns >= TL::NS) ns -= TL::NS;
-      issue_tile<TL>(a_src, b_src, (int64_t)nxt * TL::RB, lds + ns * TL::STAGE, wave);
+    for (int s = 0; s < TL::NS - 1; ++s)
+      if (s < ktiles) {
+        issue_rows<TL>(a_src, s * a_kstep, lds_a + s * TL::A_BYTES, wave);
+        issue_rows<TL>(b_src, s * b_kstep, lds_b + s * TL::B_BYTES, wave);
+      }
+    int stage = 0;
+    for (int kt = 0; kt < ktiles; ++kt) {
+      // tiles issued after tile kt: min(NS - 2, ktiles - 1 - kt)
+      const int after = min(TL::NS - 2, ktiles - 1 - kt);
+      if (TL::NS >= 5 && after >= 3)
+        wait_loads<3 * P>();
+      else if (TL::NS >= 4 && after >= 2)
+        wait_loads<2 * P>();
+      else if (TL::NS >= 3 && after >= 1)
+        wait_loads<P>();
+      else
+        wait_loads<0>();
+      const int nxt = kt + TL::NS - 1;
+      if (nxt < ktiles) {
+        int ns = stage + TL::NS - 1;
+        if (ns >= TL::NS) ns -= TL::NS;
+        issue_rows<TL>(a_src, nxt * a_kstep, lds_a + ns * TL::A_BYTES, wave);
+        issue_rows<TL>(b_src, nxt * b_kstep, lds_b + ns * TL::B_BYTES, wave);
+      }
+      compute_tile<TL>(lds_a + stage * TL::A_BYTES, lds_b + stage * TL::B_BYTES, acc, wm, wn, lane);
+      if (++stage == TL::NS) stage = 0;
     }
-    compute_tile<TL>(lds + stage * TL::STAGE, acc, wm, wn, lane);
-    if (++stage == TL::NS) stage = 0;
+  } else {
+    // 2 A stages, 3 B stages.  Issue order: A0 B0 B1 | A1 B2 | A2 B3 | ...
+    // At the top of iteration kt the last loads issued are A(kt) then
+    // B(kt+1); A(kt) and B(kt) have landed once at most B(kt+1) is pending.
+    constexpr int PB = TL::B_INS;
+    issue_rows<TL>(a_src, 0, lds_a, wave);
+    issue_rows<TL>(b_src, 0, lds_b, wave);
+    if (ktiles > 1) issue_rows<TL>(b_src, b_kstep, lds_b + TL::B_BYTES, wave);
+    int sb = 0;  // B stage of tile kt
+    for (int kt = 0; kt < ktiles; ++kt) {
+      if (kt + 1 < ktiles)
+        wait_loads<PB>();
+      else
+        wait_loads<0>();
+      if (kt + 1 < ktiles)
+        issue_rows<TL>(a_src, (kt + 1) * a_kstep, lds_a + ((kt + 1) & 1) * TL::A_BYTES, wave);
+      if (kt + 2 < ktiles) {
+        const int s2 = sb == 0 ? 2 : sb - 1;  // (kt + 2) % 3
+        issue_rows<TL>(b_src, (kt + 2) * b_kstep, lds_b + s2 * TL::B_BYTES, wave);
+      }
+      compute_tile<TL>(lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, acc, wm, wn, lane);
+      if (++sb == 3) sb = 0;
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
