@@ -94,11 +94,26 @@ def summarize_pmc(fetch_csv, write_csv, stage, workload, copy_bytes, out_path, c
     print(json.dumps(rec))
 
 
-def stage_work(w, kept, sent):
+def stage_work(w, kept, sent, dropless=False):
     """Algorithmic flops (MFMA stages) or bytes (HBM stages) per launch."""
     eb = 2 if w.dtype == "bf16" else 4
     T, D, L, E, k, F = w.T, w.d_model, w.d_latent, w.n_experts, w.top_k, w.d_ff
     S, Fs = w.n_shared, w.d_ff_shared
+    if dropless:
+        n = kept   # every valid assignment has a row
+        return {
+            "latent": ("mfma", 2.0 * T * D * L),
+            "router": ("mfma", 2.0 * T * L * E),
+            "topk": ("hbm", T * E * 4 + T * k * 8),
+            "sort": ("hbm", 2 * T * k * 4 + T * k * 4),
+            "scatter": ("hbm", T * L * eb + n * L * eb + T * k * 4),
+            "tiles": ("hbm", 0.0),
+            "expert_gate_up": ("mfma", 2.0 * n * L * 2 * F),
+            "expert_down": ("mfma", 2.0 * n * F * L),
+            "combine": ("hbm", n * L * eb + T * L * eb + 2 * T * k * 4),
+            "shared_gate_up": ("mfma", 2.0 * T * D * 2 * S * Fs),
+            "output": ("mfma", 2.0 * T * D * (L + S * Fs)),
+        }
     return {
         "latent": ("mfma", 2.0 * T * D * L),
         "router": ("mfma", 2.0 * T * L * E),
@@ -115,7 +130,7 @@ def stage_work(w, kept, sent):
     }
 
 
-def cpu_baseline(w, inp, n_tok):
+def cpu_baseline(w, inp, n_tok, dropless=False):
     """The fp64 oracle on the first n_tok tokens (its own batch: caps are
     derived for n_tok tokens), weights given as the run's bf16 values."""
     import numpy as np
@@ -141,15 +156,18 @@ def cpu_baseline(w, inp, n_tok):
                                       host["w_up"][e].to(torch.float64).numpy(),
                                       host["w_down"][e].to(torch.float64).numpy())
     t0 = time.perf_counter()
-    r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
-                       send_cap=w.send_cap, recv_cap=w.recv_cap)
+    if dropless:
+        r = oracle.forward_dropless(x, wt, top_k=w.top_k)
+    else:
+        r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
+                           send_cap=w.send_cap, recv_cap=w.recv_cap)
     dt = time.perf_counter() - t0
     assert r["y"].shape == (n_tok, w.d_model)
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": blas_threads or cores,
             "kind": "oracle",
             "sample": f"first {n_tok} tokens of the {w.name} inputs as their own batch "
-                      f"(caps for {n_tok} tokens), fp64 numpy, {dt:.1f} s wall, "
-                      f"{cores} cores in the affinity mask"}
+                      f"({'no caps' if dropless else f'caps for {n_tok} tokens'}), fp64 numpy, "
+                      f"{dt:.1f} s wall, {cores} cores in the affinity mask"}
 
 
 def main():
@@ -159,6 +177,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="marin_16k")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dropless", action="store_true",
+                    help="time the dropless ragged variant (moe_forward_dropless) instead")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
@@ -173,10 +193,11 @@ def main():
     ap.add_argument("--stage", default="expert_gate_up", help="stage for --summarize-pmc")
     ap.add_argument("--pmc-command", default="", help="command recorded by --summarize-pmc")
     args = ap.parse_args()
+    run_name = args.workload + ("_dropless" if args.dropless else "")
     if args.traffic is None:
-        args.traffic = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+        args.traffic = os.path.join(ROOT, "profiles", f"traffic_{run_name}.json")
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.stage, args.workload,
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.stage, run_name,
                       args.calib_copy_mb * 1024 * 1024, args.traffic, args.pmc_command)
         return
 
@@ -200,8 +221,15 @@ def main():
     print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w, args.seed, device=dev)
     x = inp["x"]
-    fwd = rcd.Forward(cfg, {k: v for k, v in inp.items() if k != "x"}, dev)
-    nst = rcd.stage_count()
+    weights = {k: v for k, v in inp.items() if k != "x"}
+    if args.dropless:
+        fwd = rcd.ForwardDropless(cfg, weights, dev)
+        nst = rcd.dropless_stage_count()
+        stages = rcd.abi.DROPLESS_STAGES
+    else:
+        fwd = rcd.Forward(cfg, weights, dev)
+        nst = rcd.stage_count()
+        stages = rcd.abi.STAGES
     if args.calib_copy_mb:
         n = args.calib_copy_mb * 1024 * 1024
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -209,7 +237,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    stages = rcd.abi.STAGES
     assert len(stages) == nst
 
     print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -241,7 +268,7 @@ def main():
             per[s] += ev[i][j].elapsed_time(ev[i][j + 1]) / K
     kept, sd, rd = [int(v) for v in fwd.counts.cpu().tolist()]
     sent = kept + rd
-    work = stage_work(w, kept, sent)
+    work = stage_work(w, kept, sent, dropless=args.dropless)
     peak_f = PEAK_TFLOPS[w.dtype]
     st_out = {}
     for s in stages:
@@ -270,7 +297,7 @@ def main():
     if args.traffic and os.path.exists(args.traffic):
         try:
             tr = json.load(open(args.traffic))
-            if (tr.get("stage") == dom and tr.get("workload") == w.name
+            if (tr.get("stage") == dom and tr.get("workload") == run_name
                     and tr.get("source_sha256") == kernel_source_hash()):
                 roof["traffic"] = round(tr["bytes_per_launch"])
         except (OSError, ValueError, KeyError):
@@ -291,7 +318,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_latent": w.d_latent,
+        "config": {"workload": run_name, "T": w.T, "d_model": w.d_model, "d_latent": w.d_latent,
                    "n_experts": w.n_experts, "n_pools": w.n_pools, "top_k": w.top_k,
                    "d_ff": w.d_ff, "n_shared": w.n_shared, "d_ff_shared": w.d_ff_shared,
                    "n_waves": w.n_waves, "caps": [list(w.send_cap), list(w.recv_cap)],
@@ -305,7 +332,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print(f"# cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, dropless=args.dropless)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

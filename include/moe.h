@@ -104,6 +104,11 @@ typedef struct {
   int64_t dispatch_ws_bytes; /* workspace of moe_dispatch                          */
   int64_t experts_ws_bytes;  /* workspace of moe_experts                           */
   int64_t forward_ws_bytes;  /* workspace of moe_forward (covers every tap left NULL) */
+  /* dropless ragged variant (moe_*_dropless) */
+  int64_t dropless_rows;              /* T * k: rows of xs and expert_out               */
+  int64_t dropless_dispatch_ws_bytes; /* workspace of moe_dispatch_dropless             */
+  int64_t dropless_experts_ws_bytes;  /* workspace of moe_experts_dropless              */
+  int64_t dropless_forward_ws_bytes;  /* workspace of moe_forward_dropless (taps NULL)  */
 } moe_plan;
 
 /* Weights of one branch (device pointers, element type = dtype unless noted). */
@@ -258,6 +263,85 @@ moe_status moe_forward_profiled(const moe_config* cfg, const moe_weights* w,
                                 int64_t* counts, void* ws, size_t ws_bytes,
                                 void* stream, void* const* stage_events,
                                 int32_t n_events);
+
+/* ------------------------------------------------------------------------
+ * Dropless ragged variant (lamjinlab.com section 4 and ranhao.site section
+ * 3.3: the fallback that keeps every routed assignment, a ragged all-to-all
+ * in place of the fixed capped pools; the production run switched to it).
+ * No caps, no pools, no waves: the T*k assignments are ordered by expert,
+ * stably in (token, j) order, expert e's rows form the contiguous range
+ * [expert_offsets[e], expert_offsets[e+1]) of xs and of expert_out, and the
+ * grouped GEMM runs over these variable-size groups.  The result equals the
+ * capped branch with caps large enough for every row.  bf16 only
+ * (MOE_ERR_UNSUPPORTED for MOE_F32).  n_pools, n_waves and the caps of *cfg
+ * are validated as for moe_make_plan but otherwise unused.
+ * ---------------------------------------------------------------------- */
+
+/* Optional taps of moe_forward_dropless (device pointers, each may be NULL). */
+typedef struct {
+  float* logits;           /* [T][E] fp32                              */
+  int32_t* topk_idx;       /* [T][k]                                   */
+  float* gates;            /* [T][k]                                   */
+  int32_t* row_of;         /* [T][k]: row of the assignment in xs      */
+  int32_t* expert_offsets; /* [E + 1]                                  */
+  void* z;                 /* [T][L]                                   */
+  void* xs;                /* [T*k][L] rows ordered by expert          */
+  void* expert_out;        /* [T*k][L]                                 */
+  void* y_latent;          /* [T][L]                                   */
+} moe_dropless_taps;
+
+/* Order the assignments by expert and copy their rows.
+   topk_idx (device) [T][k]; an id outside [0, E) takes no row (row_of -1)
+   and is counted in counts[1]
+   z        (device) [T][L] bf16
+   xs       (device, out) [T*k][L] bf16: row r holds z[t] of the assignment
+            (t, j) with row_of[t][j] == r; rows past expert_offsets[E] are
+            not written
+   row_of   (device, out) [T][k] int32
+   expert_offsets (device, out) [E + 1] int32, expert_offsets[0] = 0
+   counts   (device, out, may be NULL) int64[3]: {kept, invalid ids, 0}
+   ws       (device) at least dropless_dispatch_ws_bytes, 256-byte aligned. */
+moe_status moe_dispatch_dropless(const moe_config* cfg, const int32_t* topk_idx, const void* z,
+                                 void* xs, int32_t* row_of, int32_t* expert_offsets,
+                                 int64_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU over the variable-size groups: for every expert e and row r
+   of its range, expert_out[r] = (silu(xs[r] W_g[e]^T) * (xs[r] W_u[e]^T))
+   W_d[e]^T.  xs, expert_out (device) [T*k][L] bf16; expert_offsets (device)
+   [E + 1], non-decreasing with expert_offsets[E] <= T*k (not checked on the
+   device); weights as in moe_experts.  ws (device) at least
+   dropless_experts_ws_bytes, 256-byte aligned. */
+moe_status moe_experts_dropless(const moe_config* cfg, const void* xs,
+                                const int32_t* expert_offsets, const void* w_gate,
+                                const void* w_up, const void* w_down, void* expert_out, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* y_latent[t] = sum over j with row_of[t][j] >= 0 of
+   gates[t][j] * expert_out[row_of[t][j]], fp32 accumulation in j order.
+   All pointers device; y_latent [T][L] bf16 (out). */
+moe_status moe_combine_dropless(const moe_config* cfg, const void* expert_out,
+                                const int32_t* row_of, const float* gates, void* y_latent,
+                                void* stream);
+
+/* The whole branch without caps: as moe_forward, with the ragged dispatch,
+   grouped experts and combine above.  taps (host struct, may be NULL);
+   counts (device, out, may be NULL) as in moe_dispatch_dropless; ws (device)
+   at least dropless_forward_ws_bytes, 256-byte aligned. */
+moe_status moe_forward_dropless(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                                const moe_dropless_taps* taps, int64_t* counts, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Number of stages of moe_forward_dropless, in launch order: 0 latent GEMM,
+   1 router GEMM, 2 top-k and gates, 3 expert sort, 4 row scatter, 5 tile
+   lists, 6 expert gate/up GEMM, 7 expert down GEMM, 8 combine, 9
+   shared-expert gate/up GEMM, 10 output GEMM. */
+int32_t moe_forward_dropless_stage_count(void);
+
+/* moe_forward_dropless recording stage_events as moe_forward_profiled does. */
+moe_status moe_forward_dropless_profiled(const moe_config* cfg, const moe_weights* w,
+                                         const void* x, void* y, const moe_dropless_taps* taps,
+                                         int64_t* counts, void* ws, size_t ws_bytes, void* stream,
+                                         void* const* stage_events, int32_t n_events);
 
 #ifdef __cplusplus
 }

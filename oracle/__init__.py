@@ -7,7 +7,7 @@ reduce to textbook or library routines, and the constants the pages print.
 """
 from .moe_oracle import (  # noqa: F401
     assign_slots, bank_expert_rows, capacity_plan, combine, drop_fractions,
-    expert_out_pool_layout, expert_outputs, forward, gates, latent, pool_of,
-    route_topk, router_logits, selection_scores, shared_experts, silu, swiglu,
-    up_project, wave_ranges,
+    expert_out_pool_layout, expert_outputs, forward, forward_dropless, gates,
+    latent, pool_of, ragged_order, route_topk, router_logits, selection_scores,
+    shared_experts, silu, swiglu, up_project, wave_ranges,
 )

@@ -345,6 +345,61 @@ def expert_out_pool_layout(o, topk_idx, assignment, n_experts, n_pools,
 
 
 # ---------------------------------------------------------------------------
+# dropless ragged variant   [LJ §4] and [RH §3.3]: the fallback that keeps
+# every routed assignment (a ragged all-to-all instead of fixed capped pools)
+# ---------------------------------------------------------------------------
+
+
+def ragged_order(topk_idx, n_experts):
+    """Order of the T*k assignments by expert, stable in (token, j) order.
+
+    Returns (row_of [T, k], offsets [E+1]): expert e's assignments take rows
+    [offsets[e], offsets[e+1]); an id outside [0, E) takes no row (-1).
+    The order is a stable sort of the flattened expert ids (a library sort).
+    """
+    topk_idx = np.asarray(topk_idx, dtype=np.int64)
+    flat = topk_idx.reshape(-1)
+    valid = (flat >= 0) & (flat < n_experts)
+    counts = np.bincount(flat[valid], minlength=n_experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    order = np.argsort(np.where(valid, flat, n_experts), kind="stable")
+    row_of = np.full(flat.shape, -1, dtype=np.int64)
+    nv = int(valid.sum())
+    row_of[order[:nv]] = np.arange(nv)
+    return row_of.reshape(topk_idx.shape), offsets
+
+
+def forward_dropless(x, w, *, top_k, routing_logits32=None, tokens=None):
+    """The branch with every assignment kept: top-k, gates, every selected
+    expert's SwiGLU, the unrenormalised gate-weighted sum, up-projection and
+    shared experts.  Equal to forward() with caps that hold every row."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    z = latent(x[toks], w["w_latent"])
+    logits = router_logits(z, w["w_router"])
+    if routing_logits32 is None:
+        if tokens is not None:
+            raise ValueError("a token subset needs the full routing logits")
+        routing_logits32 = logits.astype(np.float32)
+    topk_idx = route_topk(routing_logits32, w["router_bias"], top_k)
+    g = gates(routing_logits32, topk_idx)
+    E = np.asarray(w["w_router"]).shape[0]
+    row_of, offsets = ragged_order(topk_idx, E)
+    ew = w.get("expert_weights")
+    if ew is None:
+        def ew(e):
+            return w["w_gate"][e], w["w_up"][e], w["w_down"][e]
+    kept = np.zeros(topk_idx.shape, dtype=np.int64)   # every row is kept
+    o = expert_outputs(z, topk_idx, kept, ew, tokens=toks)
+    y_lat = combine(g[toks], kept[toks], o)
+    y = up_project(y_lat, w["w_up_proj"]) + shared_experts(
+        x[toks], w["ws_gate"], w["ws_up"], w["ws_down"])
+    return dict(z=z, logits=logits, topk_idx=topk_idx, gates=g, row_of=row_of,
+                offsets=offsets, expert_out=o, y_latent=y_lat, y=y, tokens=toks)
+
+
+# ---------------------------------------------------------------------------
 # receive-side share of one rank: experts over a given bank, then combine
 # ---------------------------------------------------------------------------
 

@@ -15,6 +15,7 @@ import torch
 from . import abi
 
 __all__ = ["make_config", "plan", "route", "dispatch", "experts", "combine", "forward",
+           "dispatch_dropless", "experts_dropless", "combine_dropless", "forward_dropless",
            "library", "MoeError"]
 
 MoeError = abi.MoeError
@@ -212,5 +213,109 @@ def stage_count() -> int:
 def forward(cfg, weights: Dict[str, torch.Tensor], x: torch.Tensor, taps=False):
     """One forward call; returns (y, counts, taps-dict)."""
     f = Forward(cfg, weights, x.device, taps=taps)
+    y = f(x)
+    return y, f.counts, f.tap_t
+
+
+# ---------------------------------------------------------------- dropless
+
+
+def dispatch_dropless(cfg, topk_idx: torch.Tensor, z: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """Rows ordered by expert: xs [T*k, L], row_of [T, k], expert_offsets [E+1]."""
+    p = plan(cfg)
+    dev = z.device
+    T, k, E = cfg.T, cfg.top_k, cfg.n_experts
+    out = dict(
+        xs=torch.empty((p["dropless_rows"], cfg.d_latent), dtype=_tdt(cfg), device=dev),
+        row_of=torch.empty((T, k), dtype=torch.int32, device=dev),
+        expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        counts=torch.empty(3, dtype=torch.int64, device=dev),
+    )
+    ws = _ws(p["dropless_dispatch_ws_bytes"], dev)
+    abi.check("moe_dispatch_dropless", library().moe_dispatch_dropless(
+        C.byref(cfg), _ptr(topk_idx), _ptr(z), _ptr(out["xs"]), _ptr(out["row_of"]),
+        _ptr(out["expert_offsets"]), _ptr(out["counts"]), _ptr(ws), ws.numel(), _stream(dev)))
+    out["plan"] = p
+    return out
+
+
+def experts_dropless(cfg, xs, expert_offsets, w_gate, w_up, w_down, expert_out=None):
+    p = plan(cfg)
+    dev = xs.device
+    if expert_out is None:
+        expert_out = torch.empty((p["dropless_rows"], cfg.d_latent), dtype=_tdt(cfg), device=dev)
+    ws = _ws(p["dropless_experts_ws_bytes"], dev)
+    abi.check("moe_experts_dropless", library().moe_experts_dropless(
+        C.byref(cfg), _ptr(xs), _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(expert_out), _ptr(ws), ws.numel(), _stream(dev)))
+    return expert_out
+
+
+def combine_dropless(cfg, expert_out, row_of, gates, y_latent=None):
+    dev = expert_out.device
+    if y_latent is None:
+        y_latent = torch.empty((cfg.T, cfg.d_latent), dtype=_tdt(cfg), device=dev)
+    abi.check("moe_combine_dropless", library().moe_combine_dropless(
+        C.byref(cfg), _ptr(expert_out), _ptr(row_of), _ptr(gates), _ptr(y_latent), _stream(dev)))
+    return y_latent
+
+
+class ForwardDropless:
+    """Reusable dropless forward call (weights, workspace and outputs bound once)."""
+
+    def __init__(self, cfg, weights: Dict[str, torch.Tensor], device, taps=False):
+        self.cfg = cfg
+        self.p = plan(cfg)
+        self.w = weights
+        self.wstruct = abi.MoeWeights(**{n: _ptr(weights.get(n)) for n, _ in
+                                         abi.MoeWeights._fields_})
+        self.ws = _ws(self.p["dropless_forward_ws_bytes"], device)
+        self.y = torch.empty((cfg.T, cfg.d_model), dtype=_tdt(cfg), device=device)
+        self.counts = torch.empty(3, dtype=torch.int64, device=device)
+        self.taps = None
+        self.tap_t = {}
+        if taps:
+            T, k, E, L = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_latent
+            n = self.p["dropless_rows"]
+            dt = _tdt(cfg)
+            i32 = dict(dtype=torch.int32, device=device)
+            self.tap_t = dict(
+                logits=torch.empty((T, E), dtype=torch.float32, device=device),
+                topk_idx=torch.empty((T, k), **i32),
+                gates=torch.empty((T, k), dtype=torch.float32, device=device),
+                row_of=torch.empty((T, k), **i32),
+                expert_offsets=torch.empty(E + 1, **i32),
+                z=torch.empty((T, L), dtype=dt, device=device),
+                xs=torch.empty((n, L), dtype=dt, device=device),
+                expert_out=torch.empty((n, L), dtype=dt, device=device),
+                y_latent=torch.empty((T, L), dtype=dt, device=device),
+            )
+            self.taps = abi.MoeDroplessTaps(**{n_: _ptr(t) for n_, t in self.tap_t.items()})
+
+    def _taps_arg(self):
+        return C.byref(self.taps) if self.taps is not None else None
+
+    def __call__(self, x: torch.Tensor):
+        abi.check("moe_forward_dropless", library().moe_forward_dropless(
+            C.byref(self.cfg), C.byref(self.wstruct), _ptr(x), _ptr(self.y), self._taps_arg(),
+            _ptr(self.counts), _ptr(self.ws), self.ws.numel(), _stream(x.device)))
+        return self.y
+
+    def profiled(self, x: torch.Tensor, events):
+        arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+        abi.check("moe_forward_dropless_profiled", library().moe_forward_dropless_profiled(
+            C.byref(self.cfg), C.byref(self.wstruct), _ptr(x), _ptr(self.y), self._taps_arg(),
+            _ptr(self.counts), _ptr(self.ws), self.ws.numel(), _stream(x.device), arr,
+            len(events)))
+        return self.y
+
+
+def dropless_stage_count() -> int:
+    return library().moe_forward_dropless_stage_count()
+
+
+def forward_dropless(cfg, weights: Dict[str, torch.Tensor], x: torch.Tensor, taps=False):
+    """One dropless forward call; returns (y, counts, taps-dict)."""
+    f = ForwardDropless(cfg, weights, x.device, taps=taps)
     y = f(x)
     return y, f.counts, f.tap_t

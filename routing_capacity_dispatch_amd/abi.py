@@ -34,7 +34,9 @@ class MoePlan(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "tokens_per_wave", "cap_send", "cap_recv", "experts_per_pool", "elem_bytes",
         "row_bytes", "pool_block_bytes", "ids_offset", "pools_bytes", "expert_out_bytes",
-        "max_expert_rows", "dispatch_ws_bytes", "experts_ws_bytes", "forward_ws_bytes")]
+        "max_expert_rows", "dispatch_ws_bytes", "experts_ws_bytes", "forward_ws_bytes",
+        "dropless_rows", "dropless_dispatch_ws_bytes", "dropless_experts_ws_bytes",
+        "dropless_forward_ws_bytes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -50,6 +52,12 @@ class MoeTaps(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "logits", "topk_idx", "gates", "pool_slot", "recv_slot", "pool_count",
         "expert_count", "bank_rows", "z", "pools", "expert_out", "y_latent")]
+
+
+class MoeDroplessTaps(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "logits", "topk_idx", "gates", "row_of", "expert_offsets", "z", "xs", "expert_out",
+        "y_latent")]
 
 
 # exported symbols and their signatures
@@ -70,10 +78,24 @@ SIGNATURES = {
     "moe_forward_profiled": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights), _P, _P,
                                        C.POINTER(MoeTaps), _P, _P, C.c_size_t, _P,
                                        C.POINTER(C.c_void_p), C.c_int32]),
+    "moe_dispatch_dropless": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P,
+                                        C.c_size_t, _P]),
+    "moe_experts_dropless": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P,
+                                       C.c_size_t, _P]),
+    "moe_combine_dropless": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P]),
+    "moe_forward_dropless": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights), _P, _P,
+                                       C.POINTER(MoeDroplessTaps), _P, _P, C.c_size_t, _P]),
+    "moe_forward_dropless_stage_count": (C.c_int32, []),
+    "moe_forward_dropless_profiled": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights),
+                                                _P, _P, C.POINTER(MoeDroplessTaps), _P, _P,
+                                                C.c_size_t, _P, C.POINTER(C.c_void_p),
+                                                C.c_int32]),
 }
 
 STAGES = ["latent", "router", "topk", "assign", "scatter", "recv_bin", "expert_rows",
           "expert_gate_up", "expert_down", "combine", "shared_gate_up", "output"]
+DROPLESS_STAGES = ["latent", "router", "topk", "sort", "scatter", "tiles", "expert_gate_up",
+                   "expert_down", "combine", "shared_gate_up", "output"]
 
 _lib = None
 

@@ -282,10 +282,83 @@ __global__ __launch_bounds__(ExpertTile::THREADS) void expert_down_bf16_kernel(E
                 [&](int r) { return out + ((int64_t)er[r] * p.L + n0) * 2; });
 }
 
+// ------------------------------------------------------------------ ragged
+// Dropless grouped GEMMs: list entry t = (expert e, n tile, m tile); expert
+// e's rows are rows [offsets[e], offsets[e+1]) of A and of C.  XCD x runs an
+// eighth of the list, contiguous, so an expert's tiles share one L2.
+template <class TL, bool kSwiglu>
+__global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) {
+  __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
+  // the list's length is known only on the device: deal ceil(n / 8)
+  // consecutive entries to each XCD (the grid covers the longest list)
+  const int n = *p.ntiles;
+  const int per_xcd = (n + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * per_xcd + local;
+  if (local >= per_xcd || t >= n) return;
+  const int e = p.list[3 * t], nt = p.list[3 * t + 1], mt = p.list[3 * t + 2];
+  const int row0 = p.offsets[e];
+  const int rows = p.offsets[e + 1] - row0;
+  const int m0 = mt * TL::BM;
+  if (m0 >= rows) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const char* a_src[TL::A_INS];
+  const char* b_src[TL::B_INS];
+#pragma unroll
+  for (int i = 0; i < TL::A_INS; ++i) {
+    const int m = min(m0 + load_row<TL>(i, wave, lane), rows - 1);
+    a_src[i] = p.A + (int64_t)(row0 + m) * p.a_row_bytes + load_col<TL>(lane);
+  }
+  const int c0 = kSwiglu ? nt * (TL::BN / 2) : nt * TL::BN;
+#pragma unroll
+  for (int i = 0; i < TL::B_INS; ++i) {
+    const int r = load_row<TL>(i, wave, lane);
+    if (kSwiglu) {
+      int half;
+      const int f = min(c0 + swiglu_feature<TL>(r, half), p.F - 1);
+      b_src[i] = (half ? p.W1 : p.W0) + ((int64_t)e * p.F + f) * p.K * 2 + load_col<TL>(lane);
+    } else {
+      const int n = min(c0 + r, p.N - 1);
+      b_src[i] = p.W0 + ((int64_t)e * p.N + n) * p.K * 2 + load_col<TL>(lane);
+    }
+  }
+  Acc<TL> acc;
+  acc.zero();
+  mainloop<TL>(a_src, b_src, p.K / TL::BK, lds, acc);
+  const int cols = kSwiglu ? p.F : p.N;
+  const int tile_cols = kSwiglu ? TL::BN / 2 : TL::BN;
+  const int ld = tile_cols * 2 + kStagePad;
+  if (kSwiglu)
+    stage_swiglu_bf16<TL>(acc, lds, ld);
+  else
+    stage_bf16<TL>(acc, lds, ld);
+  __syncthreads();
+  const int cpr = tile_cols * 2 / 16;
+  copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0), min(cpr, (cols - c0) * 2 / 16), [&](int r) {
+    return p.C + (int64_t)(row0 + m0 + r) * p.c_row_bytes + (int64_t)c0 * 2;
+  });
+}
+
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 inline int pad8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 }  // namespace
+
+int ragged_tile_rows() { return ExpertTile::BM; }
+int ragged_gate_up_cols() { return ExpertTile::BN / 2; }
+int ragged_down_cols() { return ExpertTile::BN; }
+
+hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
+  if (max_entries <= 0) return hipSuccess;
+  ragged_gemm_kernel<ExpertTile, true><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
+  if (max_entries <= 0) return hipSuccess;
+  ragged_gemm_kernel<ExpertTile, false><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_dense_bf16(const GemmDense& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;

@@ -50,7 +50,7 @@ struct Tile {
   static constexpr int MAIN_LDS = NS * A_BYTES + NSB * B_BYTES;
   static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
   static_assert(NS >= 2 && NS <= 5, "2 to 5 stages");
-  static_assert(NSB == NS || (NS == 2 && NSB == 3), "B stages: NS, or 3 with 2 A stages");
+  static_assert(NSB == NS || (NS == 2 && (NSB == 3 || NSB == 4)), "B stages: NS, or 3-4 with 2 A stages");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows come in whole loads per wavefront");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wavefront sub-tiles are whole 16x16 blocks");
   // chunk swizzle of row r: XOR applied to the 16-byte chunk index, chosen so
@@ -155,8 +155,8 @@ __device__ __forceinline__ void wait_loads() {
 }
 
 // Accumulate K range [0, ktiles * BK) into acc.  With NS stages of A and B,
-// tiles kt+1 .. kt+NS-1 are in flight while tile kt is consumed; with 3 B
-// stages and 2 A stages, A(kt+1) and B(kt+1), B(kt+2) are.  Loads return in
+// tiles kt+1 .. kt+NS-1 are in flight while tile kt is consumed; with 2 A
+// stages and NSB B stages, A(kt+1) and B(kt+1) .. B(kt+NSB-1) are.  Loads return in
 // issue order, so waiting until at most n load instructions of a wavefront
 // are outstanding means all but its last n have landed.  Ends with a barrier
 // so the caller may reuse the LDS.
@@ -204,27 +204,42 @@ __device__ __forceinline__ void mainloop(const char* const (&a_src)[TL::A_INS],
       if (++stage == TL::NS) stage = 0;
     }
   } else {
-    // 2 A stages, 3 B stages.  Issue order: A0 B0 B1 | A1 B2 | A2 B3 | ...
-    // At the top of iteration kt the last loads issued are A(kt) then
-    // B(kt+1); A(kt) and B(kt) have landed once at most B(kt+1) is pending.
+    // 2 A stages (A one tile ahead), NSB B stages (B DB = NSB - 1 tiles
+    // ahead).  Issue order: B0 A0 B1 .. B(DB-1) | A1 B(DB) | A2 B(DB+1) | ...
+    // At the top of iteration kt >= 1 the last loads issued are A(kt) then
+    // B(kt-1+DB), and B(kt) came before A(kt): both have landed once at most
+    // the B loads after A(kt) are pending.
     constexpr int PB = TL::B_INS;
-    issue_rows<TL>(a_src, 0, lds_a, wave);
+    constexpr int DB = TL::NSB - 1;
     issue_rows<TL>(b_src, 0, lds_b, wave);
-    if (ktiles > 1) issue_rows<TL>(b_src, b_kstep, lds_b + TL::B_BYTES, wave);
+    issue_rows<TL>(a_src, 0, lds_a, wave);
+#pragma unroll
+    for (int j = 1; j < DB; ++j)
+      if (j < ktiles) issue_rows<TL>(b_src, j * b_kstep, lds_b + j * TL::B_BYTES, wave);
     int sb = 0;  // B stage of tile kt
     for (int kt = 0; kt < ktiles; ++kt) {
-      if (kt + 1 < ktiles)
+      if (kt == 0) {
+        const int pend = min(DB - 1, ktiles - 1);  // B(1) .. B(DB-1) after A(0)
+        if (DB >= 3 && pend >= 2)
+          wait_loads<2 * PB>();
+        else if (pend >= 1)
+          wait_loads<PB>();
+        else
+          wait_loads<0>();
+      } else if (kt - 1 + DB < ktiles) {
         wait_loads<PB>();
-      else
+      } else {
         wait_loads<0>();
+      }
       if (kt + 1 < ktiles)
         issue_rows<TL>(a_src, (kt + 1) * a_kstep, lds_a + ((kt + 1) & 1) * TL::A_BYTES, wave);
-      if (kt + 2 < ktiles) {
-        const int s2 = sb == 0 ? 2 : sb - 1;  // (kt + 2) % 3
-        issue_rows<TL>(b_src, (kt + 2) * b_kstep, lds_b + s2 * TL::B_BYTES, wave);
+      if (kt + DB < ktiles) {
+        int s2 = sb + DB;  // (kt + DB) % NSB
+        if (s2 >= TL::NSB) s2 -= TL::NSB;
+        issue_rows<TL>(b_src, (kt + DB) * b_kstep, lds_b + s2 * TL::B_BYTES, wave);
       }
       compute_tile<TL>(lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, acc, wm, wn, lane);
-      if (++sb == 3) sb = 0;
+      if (++sb == TL::NSB) sb = 0;
     }
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -116,4 +116,41 @@ hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s);
 
 hipError_t launch_zero_i64(int64_t* p, int n, hipStream_t s);
 
+// ---------------------------------------------------------------- dropless
+// Stable counting sort of n assignments by expert (ragged.hip): chunks of
+// kRaggedChunk assignments; hist and base are [blocks][E] int32.
+constexpr int kRaggedChunk = 4096;
+int ragged_sort_blocks(int64_t n);
+hipError_t launch_ragged_sort(const int32_t* topk, int64_t n, int E, int32_t* hist, int32_t* base,
+                              int32_t* offsets, int32_t* row_of, int64_t* counts, hipStream_t s);
+hipError_t launch_ragged_scatter(const void* z, const int32_t* row_of, int64_t T, int k, int64_t row_bytes,
+                                 void* xs, hipStream_t s);
+// Tile lists of the ragged grouped GEMMs: (expert, n tile, m tile) int32
+// triples, M tiles of bm rows; ntiles[0], ntiles[1] = entries of each list.
+hipError_t launch_ragged_tiles(const int32_t* offsets, int E, int bm, int tiles_n0, int tiles_n1,
+                               int32_t* list0, int32_t* list1, int32_t* ntiles, hipStream_t s);
+hipError_t launch_ragged_combine(int dt, const void* out, const int32_t* row_of, const float* gates, int64_t T,
+                                 int k, int64_t row_bytes, void* y, hipStream_t s);
+
+// Ragged grouped GEMMs (bf16, gemm_bf16.hip).  Expert e's rows are rows
+// [offsets[e], offsets[e+1]) of A and of C.
+struct RaggedGemm {
+  const char* A;
+  int64_t a_row_bytes;
+  const int32_t* offsets;  // [E+1]
+  const int32_t* list;     // tile list of this GEMM
+  const int32_t* ntiles;   // device: entries of the list
+  const char* W0;          // gate weights [E][F][K], or down weights [E][N][K]
+  const char* W1;          // up weights [E][F][K] (SwiGLU only)
+  int E, F, K, N;
+  char* C;
+  int64_t c_row_bytes;
+};
+// M rows per tile and N columns (features for the SwiGLU) per tile.
+int ragged_tile_rows();
+int ragged_gate_up_cols();
+int ragged_down_cols();
+hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
+hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
+
 }  // namespace moe

@@ -64,6 +64,16 @@ int64_t capacity(int64_t num, int64_t den, int64_t Tw, int64_t k, int64_t n) {
   return (int64_t)((a + b - 1) / b);
 }
 
+// Upper bounds of the ragged GEMMs' tile lists: expert e has
+// ceil(count_e / bm) <= count_e / bm + 1 M tiles.
+void dropless_entries(const moe_config* c, int64_t* ent0, int64_t* ent1) {
+  const int64_t n = c->T * (int64_t)c->top_k;
+  const int64_t bm = moe::ragged_tile_rows();
+  const int64_t mt = ceil_div(n, bm) + c->n_experts;
+  *ent0 = mt * ceil_div(c->d_ff, moe::ragged_gate_up_cols());
+  *ent1 = mt * ceil_div(c->d_latent, moe::ragged_down_cols());
+}
+
 moe_status plan_impl(const moe_config* c, moe_plan* p) {
   if (!c || !p) return MOE_ERR_INVALID_ARG;
   moe_status st = check_route_shape(c);
@@ -135,6 +145,39 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   f.take(p->dispatch_ws_bytes);
   f.take(p->experts_ws_bytes);
   p->forward_ws_bytes = f.used;
+
+  // dropless ragged variant
+  const int64_t n = T * k;
+  int64_t ent0, ent1;
+  dropless_entries(c, &ent0, &ent1);
+  if (ent0 > kI32Max / 3 || ent1 > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+  const int64_t nblk = moe::ragged_sort_blocks(n);
+  p->dropless_rows = n;
+  Carver dd{nullptr, 0};
+  dd.take(nblk * E * 4);  // per-chunk histograms
+  dd.take(nblk * E * 4);  // per-chunk bases
+  p->dropless_dispatch_ws_bytes = dd.used;
+  Carver dx{nullptr, 0};
+  dx.take(ent0 * 12);     // gate/up tile list
+  dx.take(ent1 * 12);     // down tile list
+  dx.take(8);             // list lengths
+  dx.take(n * F * eb);    // SwiGLU hidden rows
+  p->dropless_experts_ws_bytes = dx.used;
+  Carver df{nullptr, 0};
+  df.take(T * L * eb);    // z
+  df.take(T * E * 4);     // logits
+  df.take(T * k * 4);     // topk
+  df.take(T * k * 4);     // gates
+  df.take(T * k * 4);     // row_of
+  df.take((E + 1) * 4);   // expert offsets
+  df.take(n * L * eb);    // xs
+  df.take(n * L * eb);    // expert_out
+  df.take(T * L * eb);    // y_latent
+  df.take(T * S * Fs * eb);
+  df.take(3 * 8);
+  df.take(p->dropless_dispatch_ws_bytes);
+  df.take(p->dropless_experts_ws_bytes);
+  p->dropless_forward_ws_bytes = df.used;
   return MOE_OK;
 }
 
@@ -446,3 +489,235 @@ MOE_API moe_status moe_forward_profiled(const moe_config* cfg, const moe_weights
 }
 
 MOE_API int32_t moe_forward_stage_count(void) { return kStages; }
+
+// ------------------------------------------------------------------ dropless
+namespace {
+
+constexpr int kDroplessStages = 11;
+
+moe_status check_dropless(const moe_config* cfg, moe_plan* p) {
+  moe_status st = plan_impl(cfg, p);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status run_dispatch_dropless(const moe_config* c, const moe_plan& p, const int32_t* topk, const void* z,
+                                 void* xs, int32_t* row_of, int32_t* offsets, int64_t* counts, void* ws,
+                                 hipStream_t s, Marks* m) {
+  const int64_t n = p.dropless_rows;
+  const int64_t nblk = moe::ragged_sort_blocks(n);
+  Carver cv{static_cast<char*>(ws), 0};
+  int32_t* hist = static_cast<int32_t*>(cv.take(nblk * c->n_experts * 4));
+  int32_t* base = static_cast<int32_t*>(cv.take(nblk * c->n_experts * 4));
+  hipError_t e = moe::launch_ragged_sort(topk, n, c->n_experts, hist, base, offsets, row_of, counts, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e == hipSuccess) e = moe::launch_ragged_scatter(z, row_of, c->T, c->top_k, p.row_bytes, xs, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  return hip_status(e);
+}
+
+moe_status run_experts_dropless(const moe_config* c, const moe_plan& p, const void* xs,
+                                const int32_t* offsets, const void* wg, const void* wu, const void* wd,
+                                void* out, void* ws, hipStream_t s, Marks* m) {
+  int64_t ent0, ent1;
+  dropless_entries(c, &ent0, &ent1);
+  const int64_t n = p.dropless_rows;
+  Carver cv{static_cast<char*>(ws), 0};
+  int32_t* list0 = static_cast<int32_t*>(cv.take(ent0 * 12));
+  int32_t* list1 = static_cast<int32_t*>(cv.take(ent1 * 12));
+  int32_t* ntiles = static_cast<int32_t*>(cv.take(8));
+  char* H = static_cast<char*>(cv.take(n * c->d_ff * p.elem_bytes));
+  const int tn0 = (int)ceil_div(c->d_ff, moe::ragged_gate_up_cols());
+  const int tn1 = (int)ceil_div(c->d_latent, moe::ragged_down_cols());
+  hipError_t e = moe::launch_ragged_tiles(offsets, c->n_experts, moe::ragged_tile_rows(), tn0, tn1, list0,
+                                          list1, ntiles, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::RaggedGemm g{};
+  g.A = static_cast<const char*>(xs);
+  g.a_row_bytes = p.row_bytes;
+  g.offsets = offsets;
+  g.list = list0;
+  g.ntiles = ntiles;
+  g.W0 = static_cast<const char*>(wg);
+  g.W1 = static_cast<const char*>(wu);
+  g.E = c->n_experts;
+  g.F = c->d_ff;
+  g.K = c->d_latent;
+  g.N = 0;
+  g.C = H;
+  g.c_row_bytes = (int64_t)c->d_ff * p.elem_bytes;
+  e = moe::launch_ragged_gate_up_bf16(g, ent0, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::RaggedGemm d{};
+  d.A = H;
+  d.a_row_bytes = (int64_t)c->d_ff * p.elem_bytes;
+  d.offsets = offsets;
+  d.list = list1;
+  d.ntiles = ntiles + 1;
+  d.W0 = static_cast<const char*>(wd);
+  d.W1 = nullptr;
+  d.E = c->n_experts;
+  d.F = 0;
+  d.K = c->d_ff;
+  d.N = c->d_latent;
+  d.C = static_cast<char*>(out);
+  d.c_row_bytes = p.row_bytes;
+  e = moe::launch_ragged_down_bf16(d, ent1, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  return hip_status(e);
+}
+
+moe_status forward_dropless_impl(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                                 const moe_dropless_taps* taps, int64_t* counts, void* ws, size_t ws_bytes,
+                                 void* stream, void* const* events, int n_events) {
+  moe_plan p;
+  moe_status st = check_dropless(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->top_k > cfg->n_experts) return MOE_ERR_INVALID_ARG;
+  if (cfg->n_experts % 4) return MOE_ERR_UNSUPPORTED;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (!w->w_latent || !w->w_router || !w->w_gate || !w->w_up || !w->w_down || !w->w_up_proj)
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.dropless_forward_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+
+  const moe_dropless_taps none{};
+  const moe_dropless_taps& tp = taps ? *taps : none;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = cfg->T, E = cfg->n_experts, k = cfg->top_k;
+  const int64_t L = cfg->d_latent, D = cfg->d_model, S = cfg->n_shared, Fs = cfg->d_ff_shared;
+  const int64_t eb = p.elem_bytes, n = p.dropless_rows;
+  const int dt = cfg->dtype;
+
+  Carver cv{static_cast<char*>(ws), 0};
+  auto pick = [&](void* tap, int64_t bytes) {
+    void* q = cv.take(bytes);
+    return tap ? tap : q;
+  };
+  void* z = pick(tp.z, T * L * eb);
+  float* logits = static_cast<float*>(pick(tp.logits, T * E * 4));
+  int32_t* topk = static_cast<int32_t*>(pick(tp.topk_idx, T * k * 4));
+  float* gates = static_cast<float*>(pick(tp.gates, T * k * 4));
+  int32_t* row_of = static_cast<int32_t*>(pick(tp.row_of, T * k * 4));
+  int32_t* offsets = static_cast<int32_t*>(pick(tp.expert_offsets, (E + 1) * 4));
+  void* xs = pick(tp.xs, n * L * eb);
+  void* out = pick(tp.expert_out, n * L * eb);
+  void* y_lat = pick(tp.y_latent, T * L * eb);
+  void* hs = cv.take(T * S * Fs * eb);
+  int64_t* cnt = static_cast<int64_t*>(pick(counts, 3 * 8));
+  void* dws = cv.take(p.dropless_dispatch_ws_bytes);
+  void* xws = cv.take(p.dropless_experts_ws_bytes);
+
+  Marks mk{events, n_events, 0};
+  Marks* m = &mk;
+  hipError_t e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::GemmDense g{};
+  g.nseg = 1;
+  g.seg[0] = {x, D, w->w_latent, D, (int)D};
+  g.C = z;
+  g.ldc = L;
+  g.M = (int)T;
+  g.N = (int)L;
+  e = moe::launch_gemm_dense(dt, dt, g, s);
+  if (e == hipSuccess) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  g.seg[0] = {z, L, w->w_router, L, (int)L};
+  g.C = logits;
+  g.ldc = E;
+  g.N = (int)E;
+  e = moe::launch_gemm_dense(dt, moe::DT_F32, g, s);
+  if (e == hipSuccess) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_topk_gates(logits, w->router_bias, T, (int)E, (int)k, topk, gates, s);
+  if (e == hipSuccess) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  st = run_dispatch_dropless(cfg, p, topk, z, xs, row_of, offsets, cnt, dws, s, m);
+  if (st != MOE_OK) return st;
+  st = run_experts_dropless(cfg, p, xs, offsets, w->w_gate, w->w_up, w->w_down, out, xws, s, m);
+  if (st != MOE_OK) return st;
+  e = moe::launch_ragged_combine(dt, out, row_of, gates, T, (int)k, p.row_bytes, y_lat, s);
+  if (e == hipSuccess) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (S > 0) {
+    e = moe::launch_swiglu_dense(dt, x, D, w->ws_gate, w->ws_up, (int)S, (int)Fs, (int)D, (int)T, hs, S * Fs,
+                                 s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (m->mark(s) != hipSuccess) return MOE_ERR_HIP;
+  moe::GemmDense o{};
+  o.nseg = 1 + (int)S;
+  o.seg[0] = {y_lat, L, w->w_up_proj, L, (int)L};
+  for (int sh = 0; sh < S; ++sh)
+    o.seg[1 + sh] = {static_cast<const char*>(hs) + sh * Fs * eb, S * Fs,
+                     static_cast<const char*>(w->ws_down) + sh * D * Fs * eb, Fs, (int)Fs};
+  o.C = y;
+  o.ldc = D;
+  o.M = (int)T;
+  o.N = (int)D;
+  e = moe::launch_gemm_dense(dt, dt, o, s);
+  if (e == hipSuccess) e = m->mark(s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+MOE_API moe_status moe_dispatch_dropless(const moe_config* cfg, const int32_t* topk_idx, const void* z,
+                                         void* xs, int32_t* row_of, int32_t* expert_offsets,
+                                         int64_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  moe_plan p;
+  moe_status st = check_dropless(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!topk_idx || !z || !xs || !row_of)) return MOE_ERR_INVALID_ARG;
+  if (p.dropless_dispatch_ws_bytes > 0 &&
+      (!ws || (int64_t)ws_bytes < p.dropless_dispatch_ws_bytes || !aligned256(ws)))
+    return MOE_ERR_WORKSPACE;
+  return run_dispatch_dropless(cfg, p, topk_idx, z, xs, row_of, expert_offsets, counts, ws,
+                               static_cast<hipStream_t>(stream), nullptr);
+}
+
+MOE_API moe_status moe_experts_dropless(const moe_config* cfg, const void* xs, const int32_t* expert_offsets,
+                                        const void* w_gate, const void* w_up, const void* w_down,
+                                        void* expert_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_plan p;
+  moe_status st = check_dropless(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!xs || !expert_out)) return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.dropless_experts_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+  return run_experts_dropless(cfg, p, xs, expert_offsets, w_gate, w_up, w_down, expert_out, ws,
+                              static_cast<hipStream_t>(stream), nullptr);
+}
+
+MOE_API moe_status moe_combine_dropless(const moe_config* cfg, const void* expert_out, const int32_t* row_of,
+                                        const float* gates, void* y_latent, void* stream) {
+  moe_plan p;
+  moe_status st = check_dropless(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!expert_out || !row_of || !gates || !y_latent)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_ragged_combine(cfg->dtype, expert_out, row_of, gates, cfg->T, cfg->top_k,
+                                               p.row_bytes, y_latent, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_forward_dropless(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                                        const moe_dropless_taps* taps, int64_t* counts, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  return forward_dropless_impl(cfg, w, x, y, taps, counts, ws, ws_bytes, stream, nullptr, 0);
+}
+
+MOE_API int32_t moe_forward_dropless_stage_count(void) { return kDroplessStages; }
+
+MOE_API moe_status moe_forward_dropless_profiled(const moe_config* cfg, const moe_weights* w, const void* x,
+                                                 void* y, const moe_dropless_taps* taps, int64_t* counts,
+                                                 void* ws, size_t ws_bytes, void* stream,
+                                                 void* const* stage_events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && !stage_events)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+  return forward_dropless_impl(cfg, w, x, y, taps, counts, ws, ws_bytes, stream, stage_events, n_events);
+}

@@ -1,0 +1,321 @@
+// Dropless ragged dispatch: every assignment is kept.  The T*k assignments
+// are ordered by expert, stably in (token, j) order, and each one's z row is
+// copied to its position in that order, so expert e's rows are the
+// contiguous range [offsets[e], offsets[e+1]) of one buffer.  On one device
+// this permutation is what a ragged all-to-all would deliver.
+//
+// Stable counting sort in three passes over fixed chunks of the assignment
+// list: per-chunk expert histograms, a scan over chunks and experts, then
+// per-chunk ranks from wavefront match masks.  No atomics touch a result
+// that depends on order, so the output is bitwise reproducible.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSortWaves = 16;
+constexpr int kSortThreads = kSortWaves * 64;
+
+__device__ __forceinline__ int key_bits_of(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+// Pass 1: hist[blk][e] = assignments of chunk blk that name expert e.
+__global__ __launch_bounds__(kSortThreads) void ragged_hist_kernel(const int32_t* __restrict__ topk, int64_t n,
+                                                                    int E, int chunk, int32_t* __restrict__ hist) {
+  extern __shared__ int32_t h[];  // [E]
+  for (int e = threadIdx.x; e < E; e += kSortThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = min(n, lo + chunk);
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kSortThreads) {
+    const int e = topk[i];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);  // a count: order-free
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kSortThreads) hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// Pass 2 (one workgroup): base[blk][e] = offsets[e] + assignments of expert e
+// in chunks before blk; offsets = exclusive scan of the expert totals.
+__global__ __launch_bounds__(1024) void ragged_scan_kernel(const int32_t* __restrict__ hist, int nblk, int E,
+                                                            int32_t* __restrict__ base,
+                                                            int32_t* __restrict__ offsets,
+                                                            int64_t* __restrict__ counts, int64_t n) {
+  __shared__ int32_t tot[1024];
+  __shared__ int32_t part[16];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) run += hist[(int64_t)b * E + e];
+  tot[e] = e < E ? run : 0;
+  __syncthreads();
+  // exclusive scan of tot[0..1023]: per wavefront, then across wavefronts
+  const int lane = e & 63, w = e >> 6;
+  int v = tot[e];
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) part[w] = v;
+  __syncthreads();
+  if (e == 0) {
+    int s = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int t = part[i];
+      part[i] = s;
+      s += t;
+    }
+  }
+  __syncthreads();
+  const int incl = v + part[w];
+  const int excl = incl - tot[e];
+  if (e < E) {
+    offsets[e] = excl;
+    int r = excl;
+    for (int b = 0; b < nblk; ++b) {
+      base[(int64_t)b * E + e] = r;
+      r += hist[(int64_t)b * E + e];
+    }
+  }
+  if (e == E - 1) {
+    offsets[E] = incl;
+    if (counts) {
+      counts[0] = incl;      // kept: every valid assignment
+      counts[1] = n - incl;  // ids outside [0, E) take no row
+      counts[2] = 0;
+    }
+  }
+}
+
+// Pass 3: row_of[i] = base[blk][e] + rank of i among chunk blk's
+// assignments to e (wavefront ranges in order, lanes in order).
+__global__ __launch_bounds__(kSortThreads) void ragged_rank_kernel(const int32_t* __restrict__ topk, int64_t n,
+                                                                    int E, int chunk,
+                                                                    const int32_t* __restrict__ base,
+                                                                    int32_t* __restrict__ row_of) {
+  extern __shared__ int32_t hw[];  // [kSortWaves][E]
+  const int lane = threadIdx.x & 63, v = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kSortWaves * E; i += kSortThreads) hw[i] = 0;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int cn = (int)(min(n, lo + chunk) - lo);
+  const int per = ((cn + kSortThreads - 1) / kSortThreads) * 64;
+  const int wlo = min(cn, v * per), whi = min(cn, wlo + per);
+  const int ebits = key_bits_of(E);
+  const uint64_t lt = lanemask_lt();
+  // per-wavefront histograms
+  for (int it = wlo; it < whi; it += 64) {
+    const int i = it + lane;
+    const int e_in = i < whi ? topk[lo + i] : -1;
+    const bool valid = e_in >= 0 && e_in < E;
+    const uint64_t me = match_key((uint32_t)(valid ? e_in : 0), ebits, ballot64(valid));
+    if (valid && (me & lt) == 0) hw[v * E + e_in] += __popcll(me);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kSortThreads) {
+    int run = base[(int64_t)blockIdx.x * E + e];
+    for (int u = 0; u < kSortWaves; ++u) {
+      const int c = hw[u * E + e];
+      hw[u * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int it = wlo; it < whi; it += 64) {
+    const int i = it + lane;
+    const int e_in = i < whi ? topk[lo + i] : -1;
+    const bool valid = e_in >= 0 && e_in < E;
+    const uint64_t me = match_key((uint32_t)(valid ? e_in : 0), ebits, ballot64(valid));
+    int r = -1;
+    if (valid) r = hw[v * E + e_in] + __popcll(me & lt);
+    if (valid && (me & lt) == 0) hw[v * E + e_in] = r + __popcll(me);
+    if (i < whi) row_of[lo + i] = r;
+  }
+}
+
+// One wavefront per token: read the z row once, write it to each of the
+// token's sorted rows.
+__global__ __launch_bounds__(256) void ragged_scatter_kernel(const char* __restrict__ z,
+                                                              const int32_t* __restrict__ row_of, int64_t T,
+                                                              int k, int64_t row_bytes, char* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int chunks = (int)(row_bytes / 16);
+  const char* src = z + t * row_bytes;
+  for (int seg = 0; seg < chunks; seg += 64 * 8) {
+    uint4 r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = seg + i * 64 + lane;
+      if (c < chunks) r[i] = ld16(src + (int64_t)c * 16);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int row = row_of[t * k + j];
+      if (row < 0) continue;
+      char* dst = xs + (int64_t)row * row_bytes;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c < chunks) st16(dst + (int64_t)c * 16, r[i]);
+      }
+    }
+  }
+}
+
+// Tile lists of the grouped GEMMs (one workgroup, thread e = expert e):
+// expert e owns ceil(count_e / bm) M tiles; list entries are (e, n tile,
+// m tile) in that order with the M tile fastest, so the M tiles that share a
+// weight tile are neighbours.  Two lists, for two N tile counts.
+__global__ __launch_bounds__(1024) void ragged_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm,
+                                                             int tiles_n0, int tiles_n1,
+                                                             int32_t* __restrict__ list0,
+                                                             int32_t* __restrict__ list1,
+                                                             int32_t* __restrict__ ntiles) {
+  __shared__ int32_t mt[1024];
+  __shared__ int32_t part[16];
+  const int e = threadIdx.x;
+  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int m = (cnt + bm - 1) / bm;
+  mt[e] = m;
+  const int lane = e & 63, w = e >> 6;
+  int v = m;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) part[w] = v;
+  __syncthreads();
+  if (e == 0) {
+    int s = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int t = part[i];
+      part[i] = s;
+      s += t;
+    }
+  }
+  __syncthreads();
+  const int incl = v + part[w];
+  const int first = incl - m;  // M tiles before expert e
+  if (e < E) {
+    for (int nt = 0; nt < tiles_n0; ++nt)
+      for (int i = 0; i < m; ++i) {
+        int32_t* q = list0 + 3 * ((int64_t)first * tiles_n0 + nt * m + i);
+        q[0] = e;
+        q[1] = nt;
+        q[2] = i;
+      }
+    for (int nt = 0; nt < tiles_n1; ++nt)
+      for (int i = 0; i < m; ++i) {
+        int32_t* q = list1 + 3 * ((int64_t)first * tiles_n1 + nt * m + i);
+        q[0] = e;
+        q[1] = nt;
+        q[2] = i;
+      }
+  }
+  if (e == E - 1) {
+    ntiles[0] = incl * tiles_n0;
+    ntiles[1] = incl * tiles_n1;
+  }
+}
+
+// y_lat[t] = sum over j with a row of gates[t][j] * out[row_of[t][j]], fp32
+// accumulation in j order, one wavefront per token.
+template <typename T>
+__global__ __launch_bounds__(256) void ragged_combine_kernel(const char* __restrict__ out,
+                                                              const int32_t* __restrict__ row_of,
+                                                              const float* __restrict__ gates, int64_t Tn, int k,
+                                                              int64_t row_bytes, char* __restrict__ y) {
+  constexpr int EPC = Chunk<T>::kElems;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int chunks = (int)(row_bytes / 16);
+  char* dst = y + t * row_bytes;
+  for (int seg = 0; seg < chunks; seg += 64 * 8) {
+    float acc[8][EPC];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) acc[i][q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int row = row_of[t * k + j];
+      if (row < 0) continue;
+      const float g = gates[t * k + j];
+      const char* src = out + (int64_t)row * row_bytes;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c < chunks) {
+          float v[EPC];
+          unpack(ld16(src + (int64_t)c * 16), v, T{});
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g, v[q], acc[i][q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = seg + i * 64 + lane;
+      if (c < chunks) st16(dst + (int64_t)c * 16, pack(acc[i], T{}));
+    }
+  }
+}
+
+}  // namespace
+
+int ragged_sort_blocks(int64_t n) { return n <= 0 ? 0 : (int)((n + kRaggedChunk - 1) / kRaggedChunk); }
+
+hipError_t launch_ragged_sort(const int32_t* topk, int64_t n, int E, int32_t* hist, int32_t* base,
+                              int32_t* offsets, int32_t* row_of, int64_t* counts, hipStream_t s) {
+  const int nblk = ragged_sort_blocks(n);
+  if (nblk > 0) {
+    ragged_hist_kernel<<<nblk, kSortThreads, sizeof(int32_t) * E, s>>>(topk, n, E, kRaggedChunk, hist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ragged_scan_kernel<<<1, 1024, 0, s>>>(hist, nblk, E, base, offsets, counts, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nblk == 0) return e;
+  const size_t lds = sizeof(int32_t) * (size_t)kSortWaves * E;
+  if (lds >= 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(ragged_rank_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  ragged_rank_kernel<<<nblk, kSortThreads, lds, s>>>(topk, n, E, kRaggedChunk, base, row_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_ragged_scatter(const void* z, const int32_t* row_of, int64_t T, int k, int64_t row_bytes,
+                                 void* xs, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  ragged_scatter_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(static_cast<const char*>(z), row_of, T, k,
+                                                                  row_bytes, static_cast<char*>(xs));
+  return hipGetLastError();
+}
+
+hipError_t launch_ragged_tiles(const int32_t* offsets, int E, int bm, int tiles_n0, int tiles_n1,
+                               int32_t* list0, int32_t* list1, int32_t* ntiles, hipStream_t s) {
+  ragged_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, bm, tiles_n0, tiles_n1, list0, list1, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_ragged_combine(int dt, const void* out, const int32_t* row_of, const float* gates, int64_t T,
+                                 int k, int64_t row_bytes, void* y, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const char* o = static_cast<const char*>(out);
+  char* yy = static_cast<char*>(y);
+  if (dt == DT_BF16)
+    ragged_combine_kernel<bf16_t><<<blocks, 256, 0, s>>>(o, row_of, gates, T, k, row_bytes, yy);
+  else
+    ragged_combine_kernel<float><<<blocks, 256, 0, s>>>(o, row_of, gates, T, k, row_bytes, yy);
+  return hipGetLastError();
+}
+
+}  // namespace moe

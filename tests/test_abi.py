@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header():
     # sizes implied by the header's field lists (natural alignment, no packing)
     assert C.sizeof(abi.MoeConfig) == 8 + 13 * 4 + 4 + 2 * 8 + 2 * 4
-    assert C.sizeof(abi.MoePlan) == 14 * 8
+    assert C.sizeof(abi.MoePlan) == 18 * 8
     assert C.sizeof(abi.MoeWeights) == 10 * 8
     assert C.sizeof(abi.MoeTaps) == 12 * 8
 
@@ -167,3 +167,38 @@ def test_calls_validate_before_enqueue(lib):
     bad.top_k = 2
     bad.n_experts = 4096
     assert lib.moe_route(C.byref(bad), fake, nul, fake, fake, nul) == abi.MOE_ERR_UNSUPPORTED
+
+
+def test_dropless_plan_and_validation(lib):
+    w = synth.workload("marin_16k")
+    p = rcd.plan(rcd.config_of(w))
+    n = w.T * w.top_k
+    assert p["dropless_rows"] == n
+    # xs and expert_out rows plus the hidden rows are the bulk of the forward workspace
+    assert p["dropless_forward_ws_bytes"] >= 2 * n * w.d_latent * 2 + n * w.d_ff * 2
+    for k in ("dropless_dispatch_ws_bytes", "dropless_experts_ws_bytes",
+              "dropless_forward_ws_bytes"):
+        assert p[k] % 256 == 0 and p[k] > 0
+    nul = None
+    fake = C.c_void_p(0x100000)
+    f32 = rcd.config_of(synth.workload("tiny_fp32"))
+    assert lib.moe_dispatch_dropless(C.byref(f32), fake, fake, fake, fake, fake, nul, fake,
+                                     1 << 30, nul) == abi.MOE_ERR_UNSUPPORTED
+    bf = rcd.config_of(synth.workload("mid_bf16"))
+    pb = rcd.plan(bf)
+    assert lib.moe_dispatch_dropless(C.byref(bf), nul, fake, fake, fake, fake, nul, fake,
+                                     1 << 30, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_dropless(C.byref(bf), fake, fake, fake, fake, fake, nul, fake,
+                                     pb["dropless_dispatch_ws_bytes"] - 1, nul) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_experts_dropless(C.byref(bf), fake, fake, fake, fake, fake, fake, fake,
+                                    pb["dropless_experts_ws_bytes"] - 256, nul) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_experts_dropless(C.byref(bf), fake, nul, fake, fake, fake, fake, fake,
+                                    1 << 30, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_dropless(C.byref(bf), nul, fake, fake, fake, nul) == abi.MOE_ERR_INVALID_ARG
+    ww = abi.MoeWeights(*([0x100000] * 10))
+    assert lib.moe_forward_dropless(C.byref(bf), C.byref(ww), fake, fake, nul, nul, fake,
+                                    pb["dropless_forward_ws_bytes"] - 1, nul) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_dropless(C.byref(bf), nul, fake, fake, nul, nul, fake,
+                                    pb["dropless_forward_ws_bytes"], nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_dropless_stage_count() == len(abi.DROPLESS_STAGES)
+    assert lib.moe_forward_stage_count() == len(abi.STAGES)
