@@ -33,9 +33,9 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 kernel names of the stages (substrings that all must match)
 STAGE_KERNEL = {
     "latent": ("dense_bf16_kernel",),
-    "expert_gate_up": ("swiglu_bf16_kernel", "true>"),
-    "expert_down": ("expert_down_bf16_kernel",),
-    "shared_gate_up": ("swiglu_bf16_kernel", "false>"),
+    "expert_gate_up": ("ragged_gemm_kernel", "true>"),
+    "expert_down": ("ragged_gemm_kernel", "false>"),
+    "shared_gate_up": ("swiglu_bf16_kernel",),
     "output": ("dense_bf16_kernel",),
     "combine": ("combine_kernel",),
     "scatter": ("scatter_kernel",),

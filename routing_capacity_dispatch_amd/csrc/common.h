@@ -105,4 +105,28 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits, uint64_t a
   return m;
 }
 
+// Exclusive scan of one int per thread over a workgroup of 1024 threads
+// (16 wavefronts).  part: 16 ints of LDS.  *total (LDS) receives the sum.
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* part, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(x, d);
+    if (lane >= d) x += o;
+  }
+  if (lane == 63) part[w] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int t = part[i];
+      part[i] = s;
+      s += t;
+    }
+    *total = s;
+  }
+  __syncthreads();
+  return x + part[w] - v;
+}
+
 }  // namespace moe

@@ -260,6 +260,42 @@ __global__ __launch_bounds__(64) void expert_rows_kernel(const int32_t* __restri
   if (lane == 0) rows_total[e] = off;
 }
 
+// Kept rows per expert over all waves, and their exclusive scan: expert e's
+// rows are [offsets[e], offsets[e+1]) of the expert-major row order.
+__global__ __launch_bounds__(1024) void expert_offsets_kernel(const int32_t* __restrict__ expert_count, int E,
+                                                               int W, int cap_recv,
+                                                               int32_t* __restrict__ offsets) {
+  __shared__ int part[16];
+  __shared__ int total;
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E)
+    for (int w = 0; w < W; ++w) c += min(max(expert_count[(int64_t)w * E + e], 0), cap_recv);
+  const int ex = block_excl_scan_1024(c, part, &total);
+  if (e < E) offsets[e] = ex;
+  if (e == 0) offsets[E] = total;
+}
+
+// Flat pool-row index ((w * P + p) * C_send + slot) of every kept row, in
+// expert-major order (waves in order, receiver slots in order).  Counts and
+// slots are clamped to the block, so malformed lists cannot send the GEMMs
+// outside the pools.
+__global__ __launch_bounds__(64) void expert_gidx_kernel(const int32_t* __restrict__ bank_rows,
+                                                         const int32_t* __restrict__ expert_count,
+                                                         const int32_t* __restrict__ offsets, int E, int P, int W,
+                                                         int cap_send, int cap_recv, int32_t* __restrict__ gidx) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int p = e / (E / P);
+  int off = offsets[e];
+  for (int w = 0; w < W; ++w) {
+    const int c = min(max(expert_count[(int64_t)w * E + e], 0), cap_recv);
+    const int32_t* br = bank_rows + ((int64_t)w * E + e) * cap_recv;
+    const int base = (w * P + p) * cap_send;
+    for (int r = lane; r < c; r += 64) gidx[off + r] = base + min(max(br[r], 0), cap_send - 1);
+    off += c;
+  }
+}
+
 __global__ void zero_i64_kernel(int64_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -299,6 +335,17 @@ hipError_t launch_expert_rows(const int32_t* bank_rows, const int32_t* expert_co
                               int32_t* rows_total, int max_rows, hipStream_t s) {
   expert_rows_kernel<<<E, 64, 0, s>>>(bank_rows, expert_count, E, P, W, (int)cap_send,
                                       (int)cap_recv, erow, rows_total, max_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_gidx(const int32_t* bank_rows, const int32_t* expert_count, int E, int P, int W,
+                              int64_t cap_send, int64_t cap_recv, int32_t* offsets, int32_t* gidx,
+                              hipStream_t s) {
+  expert_offsets_kernel<<<1, 1024, 0, s>>>(expert_count, E, W, (int)cap_recv, offsets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  expert_gidx_kernel<<<E, 64, 0, s>>>(bank_rows, expert_count, offsets, E, P, W, (int)cap_send, (int)cap_recv,
+                                      gidx);
   return hipGetLastError();
 }
 

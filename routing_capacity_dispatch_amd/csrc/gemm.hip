@@ -365,7 +365,7 @@ hipError_t launch_swiglu_dense(int dt, const void* A, int64_t lda, const void* W
 
 hipError_t launch_expert_gate_up(int dt, const ExpertGateUp& a, hipStream_t s) {
   if (a.E <= 0 || a.max_rows <= 0) return hipSuccess;
-  if (dt == DT_BF16) return launch_expert_gate_up_bf16(a, s);
+  if (dt != DT_F32) return hipErrorInvalidValue;  // bf16 experts use the grouped kernels
   SwigluArgs p{};
   p.pools = a.pools;
   p.block_bytes = a.block_bytes;
@@ -386,7 +386,7 @@ hipError_t launch_expert_gate_up(int dt, const ExpertGateUp& a, hipStream_t s) {
 
 hipError_t launch_expert_down(int dt, const ExpertDown& a, hipStream_t s) {
   if (a.E <= 0 || a.max_rows <= 0) return hipSuccess;
-  if (dt == DT_BF16) return launch_expert_down_bf16(a, s);
+  if (dt != DT_F32) return hipErrorInvalidValue;  // bf16 experts use the grouped kernels
   const dim3 grid(cdiv(a.L, BN), cdiv(a.max_rows, BM), a.E);
   expert_down_kernel<float><<<grid, NTHR, 0, s>>>(a);
   return hipGetLastError();

@@ -1,6 +1,8 @@
 // bf16 GEMMs of the MoE branch on the gfx950 core (gemm_core.h): the dense
-// projections, the shared-expert SwiGLU, and the routed experts' gathered
-// SwiGLU and scattered down-projection.  fp32 accumulation; bf16 outputs.
+// projections, the shared-expert SwiGLU, and the routed experts' grouped
+// SwiGLU and down-projection over device-built tile lists (rows gathered
+// from the pools or read from an expert-ordered buffer, outputs scattered
+// back or written in order).  fp32 accumulation; bf16 outputs.
 //
 // Tile shapes: 256 x 256 with 8 wavefronts (64 x 128 each) for the dense
 // contractions, whose M (tokens) and N are large; 192 x 256 with 8
@@ -11,9 +13,9 @@
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
 // every kernel maps its linear block index to a tile such that one XCD gets
 // a contiguous range of tiles: a group of M panels x all N tiles for the
-// dense GEMMs, whole experts (all M and N tiles of expert e on XCD e % 8)
-// for the routed experts.  Tiles that share an operand panel then run at the
-// same time on the same L2.
+// dense GEMMs, an eighth of the expert-major tile list for the routed
+// experts.  Tiles that share an operand panel then run at the same time on
+// the same L2.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -151,16 +153,9 @@ __global__ __launch_bounds__(DenseTile::THREADS) void dense_bf16_kernel(GemmDens
 
 // ------------------------------------------------------------------ SwiGLU
 struct SwigluBf16 {
-  // dense A (shared experts): row m at A + m * lda_bytes
+  // A: row m at A + m * lda_bytes
   const char* A;
   int64_t lda_bytes;
-  // gathered A (routed experts): flat pool row erow[g][m]
-  const char* pools;
-  int64_t block_bytes, row_bytes;
-  int cap_send;
-  const int32_t* erow;
-  const int32_t* rows_total;
-  int max_rows;
   // weights [G][F][K]
   const char* Wg;
   const char* Wu;
@@ -171,30 +166,17 @@ struct SwigluBf16 {
   int64_t ldc_bytes;
 };
 
-template <class TL, bool kGather>
+template <class TL>
 __global__ __launch_bounds__(TL::THREADS) void swiglu_bf16_kernel(SwigluBf16 p) {
   __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
   const int t = xcd_order(blockIdx.x, gridDim.x);
-  int g, mt, nt;
-  if (kGather) {
-    // expert g on XCD g % 8; per XCD: experts in order, then N tile, M fastest
-    const int per_g = p.tiles_m * p.tiles_n;
-    const int per_xcd = gridDim.x >> 3;
-    const int xcd = t / per_xcd, local = t - xcd * per_xcd;
-    g = (local / per_g) * 8 + xcd;
-    if (g >= p.G) return;
-    const int r = local - (local / per_g) * per_g;
-    nt = r / p.tiles_m;
-    mt = r - nt * p.tiles_m;
-  } else {
-    const int per_g = p.tiles_m * p.tiles_n;
-    g = t / per_g;
-    if (g >= p.G) return;
-    dense_tile(t - g * per_g, p.tiles_m, p.tiles_n, mt, nt);
-  }
-  const int rows = kGather ? p.rows_total[g] : p.M;
+  const int per_g = p.tiles_m * p.tiles_n;
+  const int g = t / per_g;
+  if (g >= p.G) return;
+  int mt, nt;
+  dense_tile(t - g * per_g, p.tiles_m, p.tiles_n, mt, nt);
+  const int rows = p.M;
   const int m0 = mt * TL::BM;
-  if (m0 >= rows) return;
   const int f0 = nt * (TL::BN / 2);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const char* a_src[TL::A_INS];
@@ -202,14 +184,7 @@ __global__ __launch_bounds__(TL::THREADS) void swiglu_bf16_kernel(SwigluBf16 p) 
 #pragma unroll
   for (int i = 0; i < TL::A_INS; ++i) {
     const int m = min(m0 + load_row<TL>(i, wave, lane), rows - 1);
-    if (kGather) {
-      const int fi = p.erow[(int64_t)g * p.max_rows + m];
-      const int blk = fi / p.cap_send;
-      const int slot = fi - blk * p.cap_send;
-      a_src[i] = p.pools + blk * p.block_bytes + slot * p.row_bytes + load_col<TL>(lane);
-    } else {
-      a_src[i] = p.A + m * p.lda_bytes + load_col<TL>(lane);
-    }
+    a_src[i] = p.A + m * p.lda_bytes + load_col<TL>(lane);
   }
 #pragma unroll
   for (int i = 0; i < TL::B_INS; ++i) {
@@ -225,61 +200,10 @@ __global__ __launch_bounds__(TL::THREADS) void swiglu_bf16_kernel(SwigluBf16 p) 
   stage_swiglu_bf16<TL>(acc, lds, ld);
   __syncthreads();
   constexpr int cpr = TL::BN / 16;
-  const int valid_chunks = min(cpr, (p.F - f0) * 2 / 16);
   char* C = p.C;
-  if (kGather) {
-    copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0), valid_chunks, [&](int r) {
-      return C + (((int64_t)g * p.max_rows + m0 + r) * p.F + f0) * 2;
-    });
-  } else {
-    copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0), valid_chunks, [&](int r) {
-      return C + (int64_t)(m0 + r) * p.ldc_bytes + ((int64_t)g * p.F + f0) * 2;
-    });
-  }
-}
-
-// ------------------------------------------------------------------ expert down
-__global__ __launch_bounds__(ExpertTile::THREADS) void expert_down_bf16_kernel(ExpertDown p, int tiles_m,
-                                                                               int tiles_n) {
-  using TL = ExpertTile;
-  __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
-  const int t = xcd_order(blockIdx.x, gridDim.x);
-  const int per_e = tiles_m * tiles_n;
-  const int per_xcd = gridDim.x >> 3;
-  const int xcd = t / per_xcd, local = t - xcd * per_xcd;
-  const int e = (local / per_e) * 8 + xcd;
-  if (e >= p.E) return;
-  const int r0 = local - (local / per_e) * per_e;
-  const int nt = r0 / tiles_m, mt = r0 - nt * tiles_m;
-  const int rows = p.rows_total[e];
-  const int m0 = mt * TL::BM, n0 = nt * TL::BN;
-  if (m0 >= rows) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const char* H = static_cast<const char*>(p.H);
-  const char* Wd = static_cast<const char*>(p.Wd);
-  const char* a_src[TL::A_INS];
-  const char* b_src[TL::B_INS];
-#pragma unroll
-  for (int i = 0; i < TL::A_INS; ++i) {
-    const int m = min(m0 + load_row<TL>(i, wave, lane), rows - 1);
-    a_src[i] = H + ((int64_t)e * p.max_rows + m) * p.F * 2 + load_col<TL>(lane);
-  }
-#pragma unroll
-  for (int i = 0; i < TL::B_INS; ++i) {
-    const int n = min(n0 + load_row<TL>(i, wave, lane), p.L - 1);
-    b_src[i] = Wd + ((int64_t)e * p.L + n) * p.F * 2 + load_col<TL>(lane);
-  }
-  Acc<TL> acc;
-  acc.zero();
-  mainloop<TL>(a_src, b_src, p.F / TL::BK, lds, acc);
-  constexpr int ld = TL::BN * 2 + kStagePad;
-  stage_bf16<TL>(acc, lds, ld);
-  __syncthreads();
-  constexpr int cpr = TL::BN * 2 / 16;
-  char* out = static_cast<char*>(p.out);
-  const int32_t* er = p.erow + (int64_t)e * p.max_rows + m0;
-  copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0), min(cpr, (p.L - n0) * 2 / 16),
-                [&](int r) { return out + ((int64_t)er[r] * p.L + n0) * 2; });
+  copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0), min(cpr, (p.F - f0) * 2 / 16), [&](int r) {
+    return C + (int64_t)(m0 + r) * p.ldc_bytes + ((int64_t)g * p.F + f0) * 2;
+  });
 }
 
 // ------------------------------------------------------------------ ragged
@@ -307,7 +231,14 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
 #pragma unroll
   for (int i = 0; i < TL::A_INS; ++i) {
     const int m = min(m0 + load_row<TL>(i, wave, lane), rows - 1);
-    a_src[i] = p.A + (int64_t)(row0 + m) * p.a_row_bytes + load_col<TL>(lane);
+    if (p.a_index) {
+      const int fi = p.a_index[row0 + m];
+      const int blk = fi / p.a_block_rows;
+      const int slot = fi - blk * p.a_block_rows;
+      a_src[i] = p.A + blk * p.a_block_bytes + slot * p.a_row_bytes + load_col<TL>(lane);
+    } else {
+      a_src[i] = p.A + (int64_t)(row0 + m) * p.a_row_bytes + load_col<TL>(lane);
+    }
   }
   const int c0 = kSwiglu ? nt * (TL::BN / 2) : nt * TL::BN;
 #pragma unroll
@@ -334,8 +265,10 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
     stage_bf16<TL>(acc, lds, ld);
   __syncthreads();
   const int cpr = tile_cols * 2 / 16;
+  const int32_t* ci = p.c_index;
   copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0), min(cpr, (cols - c0) * 2 / 16), [&](int r) {
-    return p.C + (int64_t)(row0 + m0 + r) * p.c_row_bytes + (int64_t)c0 * 2;
+    const int64_t row = ci ? ci[row0 + m0 + r] : row0 + m0 + r;
+    return p.C + row * p.c_row_bytes + (int64_t)c0 * 2;
   });
 }
 
@@ -384,40 +317,7 @@ hipError_t launch_swiglu_dense_bf16(const void* A, int64_t lda, const void* Wg, 
   p.tiles_n = cdiv(F, TL::BN / 2);
   p.C = static_cast<char*>(C);
   p.ldc_bytes = ldc * 2;
-  swiglu_bf16_kernel<TL, false><<<pad8((int64_t)G * p.tiles_m * p.tiles_n), TL::THREADS, 0, s>>>(p);
-  return hipGetLastError();
-}
-
-hipError_t launch_expert_gate_up_bf16(const ExpertGateUp& a, hipStream_t s) {
-  using TL = ExpertTile;
-  if (a.E <= 0 || a.max_rows <= 0) return hipSuccess;
-  SwigluBf16 p{};
-  p.pools = a.pools;
-  p.block_bytes = a.block_bytes;
-  p.row_bytes = a.row_bytes;
-  p.cap_send = a.cap_send;
-  p.erow = a.erow;
-  p.rows_total = a.rows_total;
-  p.max_rows = a.max_rows;
-  p.Wg = static_cast<const char*>(a.Wg);
-  p.Wu = static_cast<const char*>(a.Wu);
-  p.G = a.E;
-  p.F = a.F;
-  p.K = a.L;
-  p.tiles_m = cdiv(a.max_rows, TL::BM);
-  p.tiles_n = cdiv(a.F, TL::BN / 2);
-  p.C = static_cast<char*>(a.H);
-  const int64_t blocks = 8 * (int64_t)cdiv(a.E, 8) * p.tiles_m * p.tiles_n;
-  swiglu_bf16_kernel<TL, true><<<(unsigned)blocks, TL::THREADS, 0, s>>>(p);
-  return hipGetLastError();
-}
-
-hipError_t launch_expert_down_bf16(const ExpertDown& a, hipStream_t s) {
-  using TL = ExpertTile;
-  if (a.E <= 0 || a.max_rows <= 0) return hipSuccess;
-  const int tm = cdiv(a.max_rows, TL::BM), tn = cdiv(a.L, TL::BN);
-  const int64_t blocks = 8 * (int64_t)cdiv(a.E, 8) * tm * tn;
-  expert_down_bf16_kernel<<<(unsigned)blocks, TL::THREADS, 0, s>>>(a, tm, tn);
+  swiglu_bf16_kernel<TL><<<pad8((int64_t)G * p.tiles_m * p.tiles_n), TL::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 

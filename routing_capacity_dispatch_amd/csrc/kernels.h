@@ -65,13 +65,11 @@ struct ExpertDown {
 };
 hipError_t launch_expert_down(int dt, const ExpertDown& a, hipStream_t s);
 
-// bf16 paths on the gfx950 GEMM core (gemm_bf16.hip); the generic launchers
-// above dispatch to them for bf16 inputs and outputs.
+// bf16 paths on the gfx950 GEMM core (gemm_bf16.hip); the generic dense
+// launchers above dispatch to them for bf16 inputs and outputs.
 hipError_t launch_gemm_dense_bf16(const GemmDense& g, hipStream_t s);
 hipError_t launch_swiglu_dense_bf16(const void* A, int64_t lda, const void* Wg, const void* Wu, int G,
                                     int F, int K, int M, void* C, int64_t ldc, hipStream_t s);
-hipError_t launch_expert_gate_up_bf16(const ExpertGateUp& a, hipStream_t s);
-hipError_t launch_expert_down_bf16(const ExpertDown& a, hipStream_t s);
 
 // ---------------------------------------------------------------- routing
 hipError_t launch_topk_gates(const float* logits, const float* bias, int64_t T, int E,
@@ -98,6 +96,12 @@ hipError_t launch_recv_bin(const DispatchArgs& a, int32_t* bank_rows,
 hipError_t launch_expert_rows(const int32_t* bank_rows, const int32_t* expert_count,
                               int E, int P, int W, int64_t cap_send, int64_t cap_recv,
                               int32_t* erow, int32_t* rows_total, int max_rows,
+                              hipStream_t s);
+
+// bf16 path: expert-major offsets [E+1] of the kept rows and their flat pool
+// row indices gidx [offsets[E]] (the ragged GEMMs then run over them).
+hipError_t launch_expert_gidx(const int32_t* bank_rows, const int32_t* expert_count, int E, int P, int W,
+                              int64_t cap_send, int64_t cap_recv, int32_t* offsets, int32_t* gidx,
                               hipStream_t s);
 
 // ---------------------------------------------------------------- combine
@@ -137,6 +141,14 @@ hipError_t launch_ragged_combine(int dt, const void* out, const int32_t* row_of,
 struct RaggedGemm {
   const char* A;
   int64_t a_row_bytes;
+  // optional gather of A rows: row i of the expert-major order is pool row
+  // a_index[i] = block * a_block_rows + slot, at A + block * a_block_bytes +
+  // slot * a_row_bytes (NULL: row i at A + i * a_row_bytes)
+  const int32_t* a_index;
+  int a_block_rows;
+  int64_t a_block_bytes;
+  // optional scatter of C rows: row i goes to C + c_index[i] * c_row_bytes
+  const int32_t* c_index;
   const int32_t* offsets;  // [E+1]
   const int32_t* list;     // tile list of this GEMM
   const int32_t* ntiles;   // device: entries of the list

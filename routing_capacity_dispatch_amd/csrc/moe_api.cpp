@@ -74,6 +74,17 @@ void dropless_entries(const moe_config* c, int64_t* ent0, int64_t* ent1) {
   *ent1 = mt * ceil_div(c->d_latent, moe::ragged_down_cols());
 }
 
+// Tile-list bounds of the capped path's grouped GEMMs: expert e holds at
+// most max_rows kept rows, and sum_e count_e <= E * max_rows.
+void capped_entries(const moe_config* c, int64_t max_rows, int64_t* ent0, int64_t* ent1) {
+  const int64_t bm = moe::ragged_tile_rows();
+  const int64_t E = c->n_experts;
+  const int64_t per = ceil_div(max_rows, bm);
+  const int64_t mt = per * E < ceil_div(E * max_rows, bm) + E ? per * E : ceil_div(E * max_rows, bm) + E;
+  *ent0 = mt * ceil_div(c->d_ff, moe::ragged_gate_up_cols());
+  *ent1 = mt * ceil_div(c->d_latent, moe::ragged_down_cols());
+}
+
 moe_status plan_impl(const moe_config* c, moe_plan* p) {
   if (!c || !p) return MOE_ERR_INVALID_ARG;
   moe_status st = check_route_shape(c);
@@ -122,9 +133,21 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   p->dispatch_ws_bytes = d.used;
 
   Carver x{nullptr, 0};
-  x.take(E * W * cr * 4);       // expert row lists
-  x.take(E * 4);                // rows per expert
-  x.take(E * W * cr * F * eb);  // SwiGLU hidden rows
+  if (c->dtype == MOE_BF16) {
+    int64_t e0, e1;
+    capped_entries(c, W * cr, &e0, &e1);
+    if (e0 > kI32Max / 3 || e1 > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+    x.take((E + 1) * 4);          // expert-major row offsets
+    x.take(E * W * cr * 4);       // flat pool-row index of each kept row
+    x.take(e0 * 12);              // gate/up tile list
+    x.take(e1 * 12);              // down tile list
+    x.take(8);                    // list lengths
+    x.take(E * W * cr * F * eb);  // SwiGLU hidden rows, expert-major
+  } else {
+    x.take(E * W * cr * 4);       // expert row lists
+    x.take(E * 4);                // rows per expert
+    x.take(E * W * cr * F * eb);  // SwiGLU hidden rows
+  }
   p->experts_ws_bytes = x.used;
 
   Carver f{nullptr, 0};
@@ -232,6 +255,61 @@ moe_status run_experts(const moe_config* c, const moe_plan& p, const void* pools
   const int E = c->n_experts;
   const int max_rows = (int)p.max_expert_rows;
   Carver cv{static_cast<char*>(ws), 0};
+  if (c->dtype == MOE_BF16) {
+    // expert-major row lists, then the grouped GEMMs over device-built tile
+    // lists (rows gathered from the pools, outputs scattered back to them)
+    int64_t ent0, ent1;
+    capped_entries(c, max_rows, &ent0, &ent1);
+    int32_t* offsets = static_cast<int32_t*>(cv.take((int64_t)(E + 1) * 4));
+    int32_t* gidx = static_cast<int32_t*>(cv.take((int64_t)E * max_rows * 4));
+    int32_t* list0 = static_cast<int32_t*>(cv.take(ent0 * 12));
+    int32_t* list1 = static_cast<int32_t*>(cv.take(ent1 * 12));
+    int32_t* ntiles = static_cast<int32_t*>(cv.take(8));
+    char* H = static_cast<char*>(cv.take((int64_t)E * max_rows * c->d_ff * p.elem_bytes));
+    const int tn0 = (int)ceil_div(c->d_ff, moe::ragged_gate_up_cols());
+    const int tn1 = (int)ceil_div(c->d_latent, moe::ragged_down_cols());
+    hipError_t e = moe::launch_expert_gidx(bank_rows, expert_count, E, c->n_pools, c->n_waves, p.cap_send,
+                                           p.cap_recv, offsets, gidx, s);
+    if (e == hipSuccess)
+      e = moe::launch_ragged_tiles(offsets, E, moe::ragged_tile_rows(), tn0, tn1, list0, list1, ntiles, s);
+    if (e == hipSuccess && m) e = m->mark(s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    moe::RaggedGemm g{};
+    g.A = static_cast<const char*>(pools);
+    g.a_row_bytes = p.row_bytes;
+    g.a_index = gidx;
+    g.a_block_rows = (int)p.cap_send;
+    g.a_block_bytes = p.pool_block_bytes;
+    g.offsets = offsets;
+    g.list = list0;
+    g.ntiles = ntiles;
+    g.W0 = static_cast<const char*>(wg);
+    g.W1 = static_cast<const char*>(wu);
+    g.E = E;
+    g.F = c->d_ff;
+    g.K = c->d_latent;
+    g.C = H;
+    g.c_row_bytes = (int64_t)c->d_ff * p.elem_bytes;
+    e = moe::launch_ragged_gate_up_bf16(g, ent0, s);
+    if (e == hipSuccess && m) e = m->mark(s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    moe::RaggedGemm d{};
+    d.A = H;
+    d.a_row_bytes = (int64_t)c->d_ff * p.elem_bytes;
+    d.offsets = offsets;
+    d.list = list1;
+    d.ntiles = ntiles + 1;
+    d.W0 = static_cast<const char*>(wd);
+    d.E = E;
+    d.K = c->d_ff;
+    d.N = c->d_latent;
+    d.C = static_cast<char*>(expert_out);
+    d.c_row_bytes = p.row_bytes;
+    d.c_index = gidx;
+    e = moe::launch_ragged_down_bf16(d, ent1, s);
+    if (e == hipSuccess && m) e = m->mark(s);
+    return hip_status(e);
+  }
   int32_t* erow = static_cast<int32_t*>(cv.take((int64_t)E * max_rows * 4));
   int32_t* rows_total = static_cast<int32_t*>(cv.take((int64_t)E * 4));
   void* H = cv.take((int64_t)E * max_rows * c->d_ff * p.elem_bytes);
