@@ -29,6 +29,8 @@ using core::acc_row;
 using core::load_col;
 using core::load_row;
 using core::mainloop;
+using core::RowSrc;
+using core::uniform_ptr;
 
 using DenseTile = core::Tile<256, 256, 4, 2, 64, 2>;
 using ExpertTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;
@@ -115,6 +117,8 @@ __device__ __forceinline__ void copy_rows(const char* lds, int ld, int chunks_pe
 }
 
 // ------------------------------------------------------------------ dense
+// The plain schedule: with the segment loop and the full-width epilogue the
+// mid-tile barrier schedule does not fit this kernel's registers.
 __global__ __launch_bounds__(DenseTile::THREADS) void dense_bf16_kernel(GemmDense g, int tiles_m, int tiles_n) {
   using TL = DenseTile;
   __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
@@ -128,19 +132,23 @@ __global__ __launch_bounds__(DenseTile::THREADS) void dense_bf16_kernel(GemmDens
   acc.zero();
   for (int s = 0; s < g.nseg; ++s) {
     const GemmSeg& sg = g.seg[s];
-    const char* a_src[TL::A_INS];
-    const char* b_src[TL::B_INS];
+    RowSrc<TL::A_INS> a_src;
+    RowSrc<TL::B_INS> b_src;
+    const char* A = uniform_ptr(static_cast<const char*>(sg.A));
+    const char* B = uniform_ptr(static_cast<const char*>(sg.B));
 #pragma unroll
     for (int i = 0; i < TL::A_INS; ++i) {
       const int m = min(m0 + load_row<TL>(i, wave, lane), g.M - 1);
-      a_src[i] = static_cast<const char*>(sg.A) + (int64_t)m * sg.lda * 2 + load_col<TL>(lane);
+      a_src.base[i] = A;
+      a_src.off[i] = (uint32_t)(m * sg.lda * 2) + load_col<TL>(lane);
     }
 #pragma unroll
     for (int i = 0; i < TL::B_INS; ++i) {
       const int n = min(n0 + load_row<TL>(i, wave, lane), g.N - 1);
-      b_src[i] = static_cast<const char*>(sg.B) + (int64_t)n * sg.ldb * 2 + load_col<TL>(lane);
+      b_src.base[i] = B;
+      b_src.off[i] = (uint32_t)(n * sg.ldb * 2) + load_col<TL>(lane);
     }
-    mainloop<TL>(a_src, b_src, sg.K / TL::BK, lds, acc);
+    mainloop<TL, false>(a_src, b_src, sg.K / TL::BK, lds, acc);
   }
   constexpr int ld = TL::BN * 2 + kStagePad;
   stage_bf16<TL>(acc, lds, ld);
@@ -179,19 +187,21 @@ __global__ __launch_bounds__(TL::THREADS) void swiglu_bf16_kernel(SwigluBf16 p) 
   const int m0 = mt * TL::BM;
   const int f0 = nt * (TL::BN / 2);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const char* a_src[TL::A_INS];
-  const char* b_src[TL::B_INS];
+  RowSrc<TL::A_INS> a_src;
+  RowSrc<TL::B_INS> b_src;
+  const char* A = uniform_ptr(p.A);
 #pragma unroll
   for (int i = 0; i < TL::A_INS; ++i) {
     const int m = min(m0 + load_row<TL>(i, wave, lane), rows - 1);
-    a_src[i] = p.A + m * p.lda_bytes + load_col<TL>(lane);
+    a_src.base[i] = A;
+    a_src.off[i] = (uint32_t)(m * p.lda_bytes) + load_col<TL>(lane);
   }
 #pragma unroll
   for (int i = 0; i < TL::B_INS; ++i) {
-    int half;
+    int half;  // uniform per instruction: its 8 rows lie in one 16-row block
     const int f = min(f0 + swiglu_feature<TL>(load_row<TL>(i, wave, lane), half), p.F - 1);
-    const char* W = half ? p.Wu : p.Wg;
-    b_src[i] = W + ((int64_t)g * p.F + f) * p.K * 2 + load_col<TL>(lane);
+    b_src.base[i] = uniform_ptr((half ? p.Wu : p.Wg) + (int64_t)g * p.F * p.K * 2);
+    b_src.off[i] = (uint32_t)(f * p.K * 2) + load_col<TL>(lane);
   }
   Acc<TL> acc;
   acc.zero();
@@ -226,18 +236,22 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
   const int m0 = mt * TL::BM;
   if (m0 >= rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const char* a_src[TL::A_INS];
-  const char* b_src[TL::B_INS];
+  RowSrc<TL::A_INS> a_src;
+  RowSrc<TL::B_INS> b_src;
+  // A: gathered pool rows (offsets from the pools' base) or the expert's
+  // contiguous range
+  const char* A = uniform_ptr(p.a_index ? p.A : p.A + (int64_t)row0 * p.a_row_bytes);
 #pragma unroll
   for (int i = 0; i < TL::A_INS; ++i) {
     const int m = min(m0 + load_row<TL>(i, wave, lane), rows - 1);
+    a_src.base[i] = A;
     if (p.a_index) {
       const int fi = p.a_index[row0 + m];
       const int blk = fi / p.a_block_rows;
       const int slot = fi - blk * p.a_block_rows;
-      a_src[i] = p.A + blk * p.a_block_bytes + slot * p.a_row_bytes + load_col<TL>(lane);
+      a_src.off[i] = (uint32_t)(blk * p.a_block_bytes + slot * p.a_row_bytes) + load_col<TL>(lane);
     } else {
-      a_src[i] = p.A + (int64_t)(row0 + m) * p.a_row_bytes + load_col<TL>(lane);
+      a_src.off[i] = (uint32_t)(m * p.a_row_bytes) + load_col<TL>(lane);
     }
   }
   const int c0 = kSwiglu ? nt * (TL::BN / 2) : nt * TL::BN;
@@ -245,12 +259,14 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
   for (int i = 0; i < TL::B_INS; ++i) {
     const int r = load_row<TL>(i, wave, lane);
     if (kSwiglu) {
-      int half;
+      int half;  // uniform per instruction: its 8 rows lie in one 16-row block
       const int f = min(c0 + swiglu_feature<TL>(r, half), p.F - 1);
-      b_src[i] = (half ? p.W1 : p.W0) + ((int64_t)e * p.F + f) * p.K * 2 + load_col<TL>(lane);
+      b_src.base[i] = uniform_ptr((half ? p.W1 : p.W0) + (int64_t)e * p.F * p.K * 2);
+      b_src.off[i] = (uint32_t)(f * p.K * 2) + load_col<TL>(lane);
     } else {
       const int n = min(c0 + r, p.N - 1);
-      b_src[i] = p.W0 + ((int64_t)e * p.N + n) * p.K * 2 + load_col<TL>(lane);
+      b_src.base[i] = uniform_ptr(p.W0 + (int64_t)e * p.N * p.K * 2);
+      b_src.off[i] = (uint32_t)(n * p.K * 2) + load_col<TL>(lane);
     }
   }
   Acc<TL> acc;

@@ -15,9 +15,9 @@
 // the next NS-1 tiles are in flight while one tile feeds the MFMAs (B may
 // take one stage more than A).
 //
-// Row sources are per-lane pointers, so the same mainloop serves dense
-// operands, rows gathered through an index list and interleaved gate/up
-// weight rows.
+// Row sources are per-lane offsets from per-instruction wave-uniform bases,
+// so the same mainloop serves dense operands, rows gathered through an index
+// list and interleaved gate/up weight rows.
 #pragma once
 
 #include "common.h"
@@ -50,7 +50,8 @@ struct Tile {
   static constexpr int MAIN_LDS = NS * A_BYTES + NSB * B_BYTES;
   static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
   static_assert(NS >= 2 && NS <= 5, "2 to 5 stages");
-  static_assert(NSB == NS || (NS == 2 && (NSB == 3 || NSB == 4)), "B stages: NS, or 3-4 with 2 A stages");
+  static_assert(NSB == NS || (NS == 2 && (NSB == 3 || (NSB == 4 && BK == 32))),
+                "B stages: NS, or 3 with 2 A stages (4 with K tiles of 32)");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows come in whole loads per wavefront");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wavefront sub-tiles are whole 16x16 blocks");
   // chunk swizzle of row r: XOR applied to the 16-byte chunk index, chosen so
@@ -72,14 +73,32 @@ __device__ __forceinline__ int load_col(int lane) {
   return ((lane % TL::CPR) ^ TL::swz(lane / TL::CPR)) << 4;
 }
 
+// A wave-uniform pointer, held in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Row sources of one operand tile: load instruction i of a wavefront reads
+// from base[i] (wave-uniform, scalar registers) + off[i] (per lane, 32-bit),
+// so an operand buffer addressed from one base must stay below 4 GiB.
+template <int N>
+struct RowSrc {
+  const char* base[N];
+  uint32_t off[N];
+};
+
 // One 16-byte-per-lane global -> LDS load: lane l's 16 bytes land at
 // lds_wave_base + 16 l.  Written as inline assembly so the compiler does not
 // make every later LDS read wait for it; the mainloop waits explicitly
-// (s_waitcnt vmcnt(0) + barrier) before reading a stage.
-__device__ __forceinline__ void lds_load16(const char* g, char* lds_wave_base) {
+// (s_waitcnt vmcnt(n) + barrier) before reading a stage.
+__device__ __forceinline__ void lds_load16(const char* sbase, uint32_t voff, char* lds_wave_base) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MOE_LDS char*)lds_wave_base)));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sbase)
+               : "memory", "m0");
 }
 
 template <class TL>
@@ -93,12 +112,12 @@ struct Acc {
   }
 };
 
-// Issue the loads of one K tile of A or B into one stage.  src: per-lane row
-// pointers (already offset by load_col), advanced by `koff` bytes.
+// Issue the loads of one K tile of A or B into one stage: row sources
+// advanced by `koff` bytes (wave-uniform).
 template <class TL, int N>
-__device__ __forceinline__ void issue_rows(const char* const (&src)[N], int64_t koff, char* stage, int wave) {
+__device__ __forceinline__ void issue_rows(const RowSrc<N>& src, int64_t koff, char* stage, int wave) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) lds_load16(src[i] + koff, stage + (i * TL::NW + wave) * 1024);
+  for (int i = 0; i < N; ++i) lds_load16(src.base[i] + koff, src.off[i], stage + (i * TL::NW + wave) * 1024);
 }
 
 // MFMAs of one staged K tile: fragments of K sub-step 0 are read first; the
@@ -141,6 +160,52 @@ __device__ __forceinline__ void compute_tile(const char* sa, const char* sb, Acc
   __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
 }
 
+// Fragments of one 32-wide K sub-step of a staged tile.
+template <class TL>
+struct Frags {
+  uint4 a[TL::MI];
+  uint4 b[TL::NI];
+};
+
+template <class TL>
+__device__ __forceinline__ void read_frags(const char* sa, const char* sb, int ks, Frags<TL>& f, int wm, int wn,
+                                           int lane) {
+  const char* a = sa + (wm * TL::WM + (lane & 15)) * TL::RB;
+  const char* b = sb + (wn * TL::WN + (lane & 15)) * TL::RB;
+  const int off = ((ks * 4 + (lane >> 4)) ^ TL::swz(lane & 15)) << 4;
+#pragma unroll
+  for (int mi = 0; mi < TL::MI; ++mi) f.a[mi] = ld16(a + mi * 16 * TL::RB + off);
+#pragma unroll
+  for (int ni = 0; ni < TL::NI; ++ni) f.b[ni] = ld16(b + ni * 16 * TL::RB + off);
+}
+
+template <class TL>
+__device__ __forceinline__ void mfma_frags(const Frags<TL>& f, Acc<TL>& acc) {
+#pragma unroll
+  for (int mi = 0; mi < TL::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < TL::NI; ++ni)
+      acc.v[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, f.a[mi]), __builtin_bit_cast(bf16x8_t, f.b[ni]), acc.v[mi][ni], 0, 0, 0);
+}
+
+// MFMAs on `cur` with the reads of `nxt` (sub-step ks of the staged tile at
+// sa, sb) interleaved among them.
+template <class TL>
+__device__ __forceinline__ void mfma_and_read(const Frags<TL>& cur, Acc<TL>& acc, const char* sa, const char* sb,
+                                              int ks, Frags<TL>& nxt, int wm, int wn, int lane) {
+  read_frags<TL>(sa, sb, ks, nxt, wm, wn, lane);
+  mfma_frags<TL>(cur, acc);
+  constexpr int NR = TL::MI + TL::NI;
+  constexpr int NM = TL::MI * TL::NI;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
+}
+
 // Wait until at most n load instructions of this wavefront are in flight,
 // then synchronise the workgroup.
 template <int n>
@@ -164,9 +229,12 @@ __device__ __forceinline__ void wait_loads() {
 // a_kstep / b_kstep: bytes between consecutive K tiles of one row source (the
 // tile row width for row-major operands; a whole packed tile for operands
 // stored tile by tile).
-template <class TL>
-__device__ __forceinline__ void mainloop(const char* const (&a_src)[TL::A_INS],
-                                         const char* const (&b_src)[TL::B_INS], int ktiles, char* lds,
+// kSplit selects the mid-tile barrier schedule (64-wide K tiles, 2 A
+// stages); it holds two fragment sets live, so kernels short of registers
+// take the plain schedule.
+template <class TL, bool kSplit = true>
+__device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const RowSrc<TL::B_INS>& b_src,
+                                         int ktiles, char* lds,
                                          Acc<TL>& acc, int64_t a_kstep = TL::RB, int64_t b_kstep = TL::RB) {
   constexpr int P = TL::A_INS + TL::B_INS;  // load instructions per tile per wavefront
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -174,7 +242,56 @@ __device__ __forceinline__ void mainloop(const char* const (&a_src)[TL::A_INS],
   char* lds_a = lds;
   char* lds_b = lds + TL::B_BASE;
   if (ktiles <= 0) return;
-  if constexpr (TL::NSB == TL::NS) {
+  if constexpr (kSplit && TL::KS == 2 && TL::NS == 2) {
+    // One barrier per K tile, in the middle of it: the second half's MFMAs
+    // (fragments already in registers) cover the reads of the next tile's
+    // first half, so no wavefront waits on LDS after the barrier.
+    //   phase 1: MFMAs of (kt, first half)  | reads of (kt, second half)
+    //   phase 2: wait for tile kt+1, barrier (every read of tile kt done)
+    //   phase 3: loads of A(kt+2) and B(kt+NSB) into tile kt's stages;
+    //            MFMAs of (kt, second half) | reads of (kt+1, first half)
+    // Issue order: A0 B0 A1 B1 [B2] | A2 B(NSB) | A3 B(NSB+1) | ...
+    constexpr int PB = TL::B_INS;
+    constexpr int DB = TL::NSB - 1;  // B tiles issued ahead
+    issue_rows<TL>(a_src, 0, lds_a, wave);
+    issue_rows<TL>(b_src, 0, lds_b, wave);
+    if (ktiles > 1) {
+      issue_rows<TL>(a_src, a_kstep, lds_a + TL::A_BYTES, wave);
+      issue_rows<TL>(b_src, b_kstep, lds_b + TL::B_BYTES, wave);
+    }
+    if (DB == 2 && ktiles > 2) issue_rows<TL>(b_src, 2 * b_kstep, lds_b + 2 * TL::B_BYTES, wave);
+    if (DB == 2 && ktiles > 2)
+      wait_loads<P + PB>();
+    else if (ktiles > 1)
+      wait_loads<P>();
+    else
+      wait_loads<0>();
+    Frags<TL> f0, f1;
+    read_frags<TL>(lds_a, lds_b, 0, f0, wm, wn, lane);
+    int sb = 0;  // B stage of tile kt
+    // every tile but the last: one straight-line body, so the accumulators
+    // stay in place across iterations
+    for (int kt = 0; kt + 1 < ktiles; ++kt) {
+      int sb1 = sb + 1;
+      if (sb1 == TL::NSB) sb1 = 0;
+      mfma_and_read<TL>(f0, acc, lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
+      // landed: A(kt+1), B(kt+1); may still fly: B(kt+2) when B runs 2 ahead
+      if (DB == 2 && kt + 2 < ktiles)
+        wait_loads<PB>();
+      else
+        wait_loads<0>();
+      if (kt + 2 < ktiles) issue_rows<TL>(a_src, (kt + 2) * a_kstep, lds_a + (kt & 1) * TL::A_BYTES, wave);
+      // tile kt's stages are free: they take A(kt+2) and B(kt+NSB)
+      if (kt + TL::NSB < ktiles)
+        issue_rows<TL>(b_src, (kt + TL::NSB) * b_kstep, lds_b + sb * TL::B_BYTES, wave);
+      mfma_and_read<TL>(f1, acc, lds_a + ((kt + 1) & 1) * TL::A_BYTES, lds_b + sb1 * TL::B_BYTES, 0, f0, wm, wn,
+                        lane);
+      sb = sb1;
+    }
+    const int kl = ktiles - 1;
+    mfma_and_read<TL>(f0, acc, lds_a + (kl & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
+    mfma_frags<TL>(f1, acc);
+  } else if constexpr (TL::NSB == TL::NS) {
 #pragma unroll
     for (int s = 0; s < TL::NS - 1; ++s)
       if (s < ktiles) {
