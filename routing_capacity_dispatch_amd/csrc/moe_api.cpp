@@ -116,6 +116,18 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   const int64_t L = c->d_latent, F = c->d_ff;
   const int64_t S = c->n_shared, Fs = c->d_ff_shared;
 
+  // the bf16 GEMMs address each operand buffer as a scalar base plus a
+  // 32-bit lane offset: every buffer read from one base stays below 4 GiB
+  if (c->dtype == MOE_BF16) {
+    const int64_t kLim = int64_t(1) << 32;
+    const int64_t D = c->d_model;
+    const int64_t pools = W * P * align256(cs * L * 2 + cs * 4);
+    const int64_t widest = D > L ? D : L;
+    if (T * widest * 2 >= kLim || T * S * Fs * 2 >= kLim || pools >= kLim || F * L * 2 >= kLim ||
+        L * D * 2 >= kLim || Fs * D * 2 >= kLim)
+      return MOE_ERR_UNSUPPORTED;
+  }
+
   p->tokens_per_wave = Tw;
   p->cap_send = cs;
   p->cap_recv = cr;

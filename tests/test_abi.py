@@ -202,3 +202,13 @@ def test_dropless_plan_and_validation(lib):
                                     pb["dropless_forward_ws_bytes"], nul) == abi.MOE_ERR_INVALID_ARG
     assert lib.moe_forward_dropless_stage_count() == len(abi.DROPLESS_STAGES)
     assert lib.moe_forward_stage_count() == len(abi.STAGES)
+
+
+def test_bf16_operands_above_4gib_unsupported(lib):
+    # x of 350,000 tokens x 6144 bf16 is 4.3 GB: past the GEMMs' 32-bit lane offsets
+    cfg = rcd.make_config(350_000, 6144, 3072, 384, 64, 8, 3072, n_shared=2, d_ff_shared=3072,
+                          dtype="bf16")
+    assert _status(lambda: rcd.plan(cfg)) == abi.MOE_ERR_UNSUPPORTED
+    ok = rcd.make_config(65536, 6144, 3072, 384, 64, 8, 3072, n_shared=2, d_ff_shared=3072,
+                         dtype="bf16")
+    assert rcd.plan(ok)["pools_bytes"] < 2 ** 32
