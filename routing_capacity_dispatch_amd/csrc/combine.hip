@@ -1,7 +1,8 @@
 // Gate-weighted combine: y_lat[t] = sum over receiver-kept j of
 // g[t,j] * expert_out[row(t,j)], fp32 accumulation in j order, no
-// renormalisation of the gates.  One wavefront per token, 16-byte chunks,
-// up to 8 chunks per lane per pass.
+// renormalisation of the gates.  One wavefront per token: its lanes load the
+// token's k assignments at once, then the rows are read two at a time in
+// 16-byte chunks.
 #include "common.h"
 #include "kernels.h"
 
@@ -10,46 +11,25 @@ namespace {
 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  constexpr int EPC = Chunk<T>::kElems;  // elements per 16-byte chunk
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int k = a.k, epp = a.E / a.P;
   const int64_t w = t / a.Tw;
-  const int chunks = (int)(a.row_bytes / 16);
-  char* dst = static_cast<char*>(a.y) + t * a.row_bytes;
-  for (int seg = 0; seg < chunks; seg += 64 * 8) {
-    float acc[8][EPC];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int q = 0; q < EPC; ++q) acc[i][q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      if (a.recv_slot[t * k + j] < 0) continue;
-      const int e = a.topk[t * k + j];
-      const int ps = a.pool_slot[t * k + j];
-      if (e < 0 || e >= a.E || ps < 0 || ps >= a.cap_send) continue;  // malformed: skipped
-      const float g = a.gates[t * k + j];
-      const int p = e / epp;
-      const int64_t row = (w * a.P + p) * a.cap_send + ps;
-      const char* src = a.expert_out + row * a.row_bytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = seg + i * 64 + lane;
-        if (c < chunks) {
-          float v[EPC];
-          unpack(ld16(src + (int64_t)c * 16), v, T{});
-#pragma unroll
-          for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g, v[q], acc[i][q]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = seg + i * 64 + lane;
-      if (c < chunks) st16(dst + (int64_t)c * 16, pack(acc[i], T{}));
+  // lane j < k: the pool row and gate of the token's assignment j, all
+  // loaded at once (an assignment whose expert id or pool slot is out of
+  // range adds nothing)
+  int64_t row = -1;
+  float g = 0.0f;
+  if (lane < k) {
+    const int64_t q = t * k + lane;
+    const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
+    if (rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send) {
+      row = (w * a.P + e / epp) * a.cap_send + ps;
+      g = a.gates[q];
     }
   }
+  combine_rows<T>(a.expert_out, row, g, k, a.row_bytes, static_cast<char*>(a.y) + t * a.row_bytes);
 }
 
 }  // namespace

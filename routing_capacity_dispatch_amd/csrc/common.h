@@ -105,6 +105,89 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits, uint64_t a
   return m;
 }
 
+// Lane `src`'s 64-bit value, broadcast to the wavefront.
+__device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
+  const uint32_t lo = __shfl(static_cast<uint32_t>(v), src);
+  const uint32_t hi = __shfl(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32), src);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// One wavefront: dst = sum over j < k of g_j * rows[r_j], where lane j holds
+// (r_j, g_j) in (row, g) and r_j < 0 adds nothing; fp32 accumulation in j
+// order, stored as T.  Rows are row_bytes (a multiple of 16) apart from
+// base.  Two rows' loads are in flight per step.
+template <typename T>
+__device__ __forceinline__ void combine_rows(const char* __restrict__ base, int64_t row, float g, int k,
+                                             int64_t row_bytes, char* __restrict__ dst) {
+  constexpr int EPC = Chunk<T>::kElems;
+  const int lane = threadIdx.x & 63;
+  const int chunks = (int)(row_bytes / 16);
+  for (int seg = 0; seg < chunks; seg += 64 * 8) {
+    float acc[8][EPC];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) acc[i][q] = 0.0f;
+    for (int j = 0; j < k; j += 2) {
+      const int64_t r0 = shfl64(row, j);
+      const int64_t r1 = j + 1 < k ? shfl64(row, j + 1) : -1;
+      const float g0 = __shfl(g, j), g1 = __shfl(g, j + 1);
+      uint4 v0[8], v1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c < chunks && r0 >= 0) v0[i] = ld16(base + r0 * row_bytes + (int64_t)c * 16);
+        if (c < chunks && r1 >= 0) v1[i] = ld16(base + r1 * row_bytes + (int64_t)c * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c >= chunks) continue;
+        float f[EPC];
+        if (r0 >= 0) {
+          unpack(v0[i], f, T{});
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g0, f[q], acc[i][q]);
+        }
+        if (r1 >= 0) {
+          unpack(v1[i], f, T{});
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g1, f[q], acc[i][q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = seg + i * 64 + lane;
+      if (c < chunks) st16(dst + (int64_t)c * 16, pack(acc[i], T{}));
+    }
+  }
+}
+
+// One wavefront: copy the row at src to each destination named by lanes
+// 0..k-1 (dst_j = nullptr: none).  16-byte chunks.
+__device__ __forceinline__ void scatter_row(const char* __restrict__ src, char* dst, int k, int64_t row_bytes) {
+  const int lane = threadIdx.x & 63;
+  const int chunks = (int)(row_bytes / 16);
+  for (int seg = 0; seg < chunks; seg += 64 * 8) {
+    uint4 r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = seg + i * 64 + lane;
+      if (c < chunks) r[i] = ld16(src + (int64_t)c * 16);
+    }
+    for (int j = 0; j < k; ++j) {
+      char* d = reinterpret_cast<char*>(shfl64(reinterpret_cast<int64_t>(dst), j));
+      if (!d) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c < chunks) st16(d + (int64_t)c * 16, r[i]);
+      }
+    }
+  }
+}
+
 // Exclusive scan of one int per thread over a workgroup of 1024 threads
 // (16 wavefronts).  part: 16 ints of LDS.  *total (LDS) receives the sum.
 __device__ __forceinline__ int block_excl_scan_1024(int v, int* part, int* total) {

@@ -175,35 +175,23 @@ __global__ void finalize_counts_kernel(const int64_t* wave_counts, int W, int64_
   }
 }
 
-// One wavefront per token: read the z row once, write it to every pool slot
-// the token's assignments took.  16-byte chunks, up to 8 per lane at a time.
+// One wavefront per token: its lanes load the token's k pool slots at once,
+// then the z row is read once and written to every slot the token took.
 __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a, const char* __restrict__ z) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int k = a.k, epp = a.E / a.P;
   const int64_t w = t / a.Tw;
-  const int chunks = (int)(a.row_bytes / 16);
-  const char* src = z + t * a.row_bytes;
-  for (int seg = 0; seg < chunks; seg += 64 * 8) {
-    uint4 r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = seg + i * 64 + lane;
-      if (c < chunks) r[i] = ld16(src + (int64_t)c * 16);
-    }
-    for (int j = 0; j < k; ++j) {
-      const int ps = a.pool_slot[t * k + j];
-      if (ps < 0) continue;
-      const int p = a.topk[t * k + j] / epp;
-      char* dst = a.pools + (w * a.P + p) * a.block_bytes + (int64_t)ps * a.row_bytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = seg + i * 64 + lane;
-        if (c < chunks) st16(dst + (int64_t)c * 16, r[i]);
-      }
+  char* dst = nullptr;
+  if (lane < k) {
+    const int ps = a.pool_slot[t * k + lane];
+    if (ps >= 0) {
+      const int p = a.topk[t * k + lane] / epp;
+      dst = a.pools + (w * a.P + p) * a.block_bytes + (int64_t)ps * a.row_bytes;
     }
   }
+  scatter_row(z + t * a.row_bytes, dst, k, a.row_bytes);
 }
 
 // Receiver side: one wavefront per (wave, pool) block reads only the id

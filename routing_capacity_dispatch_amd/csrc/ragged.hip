@@ -137,34 +137,20 @@ __global__ __launch_bounds__(kSortThreads) void ragged_rank_kernel(const int32_t
   }
 }
 
-// One wavefront per token: read the z row once, write it to each of the
-// token's sorted rows.
+// One wavefront per token: its lanes load the token's k rows at once, then
+// the z row is read once and written to each of them.
 __global__ __launch_bounds__(256) void ragged_scatter_kernel(const char* __restrict__ z,
                                                               const int32_t* __restrict__ row_of, int64_t T,
                                                               int k, int64_t row_bytes, char* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int chunks = (int)(row_bytes / 16);
-  const char* src = z + t * row_bytes;
-  for (int seg = 0; seg < chunks; seg += 64 * 8) {
-    uint4 r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = seg + i * 64 + lane;
-      if (c < chunks) r[i] = ld16(src + (int64_t)c * 16);
-    }
-    for (int j = 0; j < k; ++j) {
-      const int row = row_of[t * k + j];
-      if (row < 0) continue;
-      char* dst = xs + (int64_t)row * row_bytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = seg + i * 64 + lane;
-        if (c < chunks) st16(dst + (int64_t)c * 16, r[i]);
-      }
-    }
+  char* dst = nullptr;
+  if (lane < k) {
+    const int row = row_of[t * k + lane];
+    if (row >= 0) dst = xs + (int64_t)row * row_bytes;
   }
+  scatter_row(z + t * row_bytes, dst, k, row_bytes);
 }
 
 // Tile lists of the grouped GEMMs (one workgroup, thread e = expert e):
@@ -230,40 +216,16 @@ __global__ __launch_bounds__(256) void ragged_combine_kernel(const char* __restr
                                                               const int32_t* __restrict__ row_of,
                                                               const float* __restrict__ gates, int64_t Tn, int k,
                                                               int64_t row_bytes, char* __restrict__ y) {
-  constexpr int EPC = Chunk<T>::kElems;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  const int chunks = (int)(row_bytes / 16);
-  char* dst = y + t * row_bytes;
-  for (int seg = 0; seg < chunks; seg += 64 * 8) {
-    float acc[8][EPC];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int q = 0; q < EPC; ++q) acc[i][q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int row = row_of[t * k + j];
-      if (row < 0) continue;
-      const float g = gates[t * k + j];
-      const char* src = out + (int64_t)row * row_bytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = seg + i * 64 + lane;
-        if (c < chunks) {
-          float v[EPC];
-          unpack(ld16(src + (int64_t)c * 16), v, T{});
-#pragma unroll
-          for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g, v[q], acc[i][q]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = seg + i * 64 + lane;
-      if (c < chunks) st16(dst + (int64_t)c * 16, pack(acc[i], T{}));
-    }
+  int64_t row = -1;
+  float g = 0.0f;
+  if (lane < k) {
+    row = row_of[t * k + lane];
+    if (row >= 0) g = gates[t * k + lane];
   }
+  combine_rows<T>(out, row, g, k, row_bytes, y + t * row_bytes);
 }
 
 }  // namespace

@@ -198,18 +198,22 @@ def test_forward_dropless_deterministic_and_profiled():
     assert all(ev[i].elapsed_time(ev[i + 1]) >= 0 for i in range(len(ev) - 1))
 
 
-def test_forward_dropless_full_size_sampled():
-    """Marin-shaped layer without caps: all integer results in full, values on
-    sampled tokens."""
+@pytest.mark.parametrize("name", ["marin_16k", "zipf_64k"])
+def test_forward_dropless_full_size_sampled(name):
+    """Full-size layers without caps: all integer results in full, values on
+    sampled tokens.  Under the Zipf bias the head experts hold thousands of
+    rows (many M tiles) and the tail experts few."""
     d = dev()
-    w = synth.workload("marin_16k")
-    say("forward dropless full size")
+    w = synth.workload(name)
+    say("forward dropless full size", name)
     inp = synth.make_inputs(w, 0, device=d)
     y, counts, taps = rcd.forward_dropless(rcd.config_of(w), {k: v for k, v in inp.items() if k != "x"},
                                            inp["x"], taps=True)
     torch.cuda.synchronize()
     rng = np.random.default_rng(2)
     toks = np.sort(rng.choice(w.T, 6, replace=False))
+    offs = np_i(taps["expert_offsets"])
+    say("largest expert group", int(np.diff(offs).max()), "rows")
     wt = {k: f64(inp[k]) for k in ("w_latent", "w_router", "w_up_proj", "ws_gate", "ws_up", "ws_down")}
     wt["router_bias"] = inp["router_bias"].cpu().numpy().astype(np.float32)
     cache = {}
