@@ -206,6 +206,40 @@ __device__ __forceinline__ void mfma_and_read(const Frags<TL>& cur, Acc<TL>& acc
   __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
 }
 
+// MFMAs on `cur` and the reads of `nxt` (sub-step ks of the staged tile at
+// sa, sb), with P load instructions issue(0) .. issue(P-1) spread among them:
+// the loads of a workgroup then reach the memory pipeline over the whole
+// phase instead of in one burst that holds up the MFMAs queued behind it.
+// Each load sits between two fragment reads in program order (the inline
+// assembly is a memory barrier to the compiler), and the reads are
+// interleaved with the MFMAs.
+template <class TL, int P, class F>
+__device__ __forceinline__ void mfma_read_issue(const Frags<TL>& cur, Acc<TL>& acc, const char* sa, const char* sb,
+                                                int ks, Frags<TL>& nxt, int wm, int wn, int lane, F&& issue) {
+  constexpr int NR = TL::MI + TL::NI, NM = TL::MI * TL::NI;
+  const char* a = sa + (wm * TL::WM + (lane & 15)) * TL::RB;
+  const char* b = sb + (wn * TL::WN + (lane & 15)) * TL::RB;
+  const int off = ((ks * 4 + (lane >> 4)) ^ TL::swz(lane & 15)) << 4;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (r < TL::MI)
+      nxt.a[r] = ld16(a + r * 16 * TL::RB + off);
+    else
+      nxt.b[r - TL::MI] = ld16(b + (r - TL::MI) * 16 * TL::RB + off);
+    // loads s with floor(s * NR / P) == r follow read r
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+      if (s * NR / P == r) issue(s);
+  }
+  mfma_frags<TL>(cur, acc);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
+}
+
 // Wait until at most n load instructions of this wavefront are in flight,
 // then synchronise the workgroup.
 template <int n>
@@ -269,19 +303,43 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
     Frags<TL> f0, f1;
     read_frags<TL>(lds_a, lds_b, 0, f0, wm, wn, lane);
     int sb = 0;  // B stage of tile kt
-    // every tile but the last: one straight-line body, so the accumulators
-    // stay in place across iterations
-    for (int kt = 0; kt + 1 < ktiles; ++kt) {
+    int kt = 0;
+    // every load of the iteration is in range: A(kt+2), B(kt+NSB), issued
+    // among the second half's MFMAs.  Each loop body is straight-line, so
+    // the accumulators stay in place across iterations.
+    for (; kt + TL::NSB < ktiles; ++kt) {
       int sb1 = sb + 1;
       if (sb1 == TL::NSB) sb1 = 0;
       mfma_and_read<TL>(f0, acc, lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
       // landed: A(kt+1), B(kt+1); may still fly: B(kt+2) when B runs 2 ahead
+      if (DB == 2)
+        wait_loads<PB>();
+      else
+        wait_loads<0>();
+      // tile kt's stages are free: they take A(kt+2) and B(kt+NSB)
+      const int64_t ka = (kt + 2) * a_kstep, kb = (kt + TL::NSB) * b_kstep;
+      char* da = lds_a + (kt & 1) * TL::A_BYTES + wave * 1024;
+      char* db = lds_b + sb * TL::B_BYTES + wave * 1024;
+      mfma_read_issue<TL, TL::A_INS + TL::B_INS>(
+          f1, acc, lds_a + ((kt + 1) & 1) * TL::A_BYTES, lds_b + sb1 * TL::B_BYTES, 0, f0, wm, wn, lane, [&](int s) {
+            if (s < TL::A_INS)
+              lds_load16(a_src.base[s] + ka, a_src.off[s], da + s * TL::NW * 1024);
+            else
+              lds_load16(b_src.base[s - TL::A_INS] + kb, b_src.off[s - TL::A_INS],
+                         db + (s - TL::A_INS) * TL::NW * 1024);
+          });
+      sb = sb1;
+    }
+    // the last NSB - 1 iterations: loads only while in range
+    for (; kt + 1 < ktiles; ++kt) {
+      int sb1 = sb + 1;
+      if (sb1 == TL::NSB) sb1 = 0;
+      mfma_and_read<TL>(f0, acc, lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
       if (DB == 2 && kt + 2 < ktiles)
         wait_loads<PB>();
       else
         wait_loads<0>();
       if (kt + 2 < ktiles) issue_rows<TL>(a_src, (kt + 2) * a_kstep, lds_a + (kt & 1) * TL::A_BYTES, wave);
-      // tile kt's stages are free: they take A(kt+2) and B(kt+NSB)
       if (kt + TL::NSB < ktiles)
         issue_rows<TL>(b_src, (kt + TL::NSB) * b_kstep, lds_b + sb * TL::B_BYTES, wave);
       mfma_and_read<TL>(f1, acc, lds_a + ((kt + 1) & 1) * TL::A_BYTES, lds_b + sb1 * TL::B_BYTES, 0, f0, wm, wn,
@@ -299,7 +357,7 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
         issue_rows<TL>(b_src, s * b_kstep, lds_b + s * TL::B_BYTES, wave);
       }
     int stage = 0;
-    for (int kt = 0; kt < ktiles; ++kt) {
+    auto wait_tile = [&](int kt) {
       // tiles issued after tile kt: min(NS - 2, ktiles - 1 - kt)
       const int after = min(TL::NS - 2, ktiles - 1 - kt);
       if (TL::NS >= 5 && after >= 3)
@@ -310,6 +368,36 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
         wait_loads<P>();
       else
         wait_loads<0>();
+    };
+    int kt = 0;
+    if constexpr (TL::KS == 2) {
+      // tile kt + NS - 1 exists: its loads go in among tile kt's MFMAs
+      for (; kt + TL::NS - 1 < ktiles; ++kt) {
+        wait_tile(kt);
+        const int nxt = kt + TL::NS - 1;
+        int ns = stage + TL::NS - 1;
+        if (ns >= TL::NS) ns -= TL::NS;
+        const int64_t ka = nxt * a_kstep, kb = nxt * b_kstep;
+        char* da = lds_a + ns * TL::A_BYTES + wave * 1024;
+        char* db = lds_b + ns * TL::B_BYTES + wave * 1024;
+        const char* sa = lds_a + stage * TL::A_BYTES;
+        const char* sb = lds_b + stage * TL::B_BYTES;
+        Frags<TL> f0, f1;
+        read_frags<TL>(sa, sb, 0, f0, wm, wn, lane);
+        __builtin_amdgcn_sched_group_barrier(0x100, TL::MI + TL::NI, 0);
+        mfma_read_issue<TL, P>(f0, acc, sa, sb, 1, f1, wm, wn, lane, [&](int s) {
+          if (s < TL::A_INS)
+            lds_load16(a_src.base[s] + ka, a_src.off[s], da + s * TL::NW * 1024);
+          else
+            lds_load16(b_src.base[s - TL::A_INS] + kb, b_src.off[s - TL::A_INS], db + (s - TL::A_INS) * TL::NW * 1024);
+        });
+        mfma_frags<TL>(f1, acc);
+        __builtin_amdgcn_sched_group_barrier(0x008, TL::MI * TL::NI, 0);
+        if (++stage == TL::NS) stage = 0;
+      }
+    }
+    for (; kt < ktiles; ++kt) {
+      wait_tile(kt);
       const int nxt = kt + TL::NS - 1;
       if (nxt < ktiles) {
         int ns = stage + TL::NS - 1;
