@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the pooled-wave capacity-dispatch MoE forward.
+"""fp64 CPU oracle of the pooled-wave capacity-dispatch MoE forward and of
+the backward of its routed path.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path.  Every function is
@@ -10,4 +11,8 @@ from .moe_oracle import (  # noqa: F401
     expert_out_pool_layout, expert_outputs, forward, forward_dropless, gates,
     latent, pool_of, ragged_order, route_topk, router_logits, selection_scores,
     shared_experts, silu, swiglu, up_project, wave_ranges,
+)
+from .moe_backward import (  # noqa: F401
+    combine_backward, dispatch_backward, experts_backward, gates_backward,
+    routed_backward, scatter_logit_grad, swiglu_backward,
 )

@@ -162,3 +162,64 @@ def test_wrong_pool_map_is_caught(monkeypatch):
         return a
     monkeypatch.setattr(oracle, "assign_slots", strided_pools)
     assert _fails(ta.test_closed_forms_tiny_workload, 0)
+
+
+# --- backward of the routed path -------------------------------------------
+
+import oracle.moe_backward as ob  # noqa: E402
+import test_oracle_backward as tb  # noqa: E402
+
+
+def test_silu_derivative_without_the_a_term_is_caught(monkeypatch):
+    def wrong(u, w_gate, w_up, w_down, d_o):
+        u, wg, wu, wd, d_o = (np.asarray(x, dtype=np.float64) for x in (u, w_gate, w_up, w_down, d_o))
+        a, b = u @ wg.T, u @ wu.T
+        s = 1 / (1 + np.exp(-a))
+        h = a * s * b
+        dh = d_o @ wd
+        da = dh * b * s          # drops the a (1 - s) term of silu'
+        db = dh * a * s
+        return da @ wg + db @ wu, da.T @ u, db.T @ u, d_o.T @ h
+    monkeypatch.setattr(ob, "swiglu_backward", wrong)
+    monkeypatch.setattr(oracle, "swiglu_backward", wrong)
+    assert _fails(tb.test_dz_matches_finite_differences, 0)
+    assert _fails(tb.test_swiglu_backward_matches_torch_autograd)
+
+
+def test_transposed_down_gradient_is_caught(monkeypatch):
+    real = ob.swiglu_backward
+
+    def wrong(*a):
+        du, dwg, dwu, dwd = real(*a)
+        return du, dwg, dwu, dwd[::-1].copy()   # rows of dW_d out of order
+    monkeypatch.setattr(ob, "swiglu_backward", wrong)
+    assert _fails(tb.test_weight_gradients_match_finite_differences, "wd")
+
+
+def test_gate_left_out_of_d_o_is_caught(monkeypatch):
+    def wrong(gate_w, recv_slot, o, dy_lat):
+        keep = (np.asarray(recv_slot) >= 0).astype(np.float64)
+        dy = np.asarray(dy_lat, dtype=np.float64)
+        d_gates = np.einsum("tl,tjl->tj", dy, np.asarray(o, dtype=np.float64)) * keep
+        return d_gates, keep[:, :, None] * dy[:, None, :]
+    monkeypatch.setattr(ob, "combine_backward", wrong)
+    assert _fails(tb.test_dz_matches_finite_differences, 1)
+
+
+def test_softmax_backward_sign_is_caught(monkeypatch):
+    def wrong(gate_w, d_gates):
+        g, dg = np.asarray(gate_w), np.asarray(d_gates)
+        return g * (dg + (g * dg).sum(axis=1, keepdims=True))
+    monkeypatch.setattr(ob, "gates_backward", wrong)
+    monkeypatch.setattr(oracle, "gates_backward", wrong)
+    assert _fails(tb.test_logit_gradient_matches_finite_differences, 0)
+    assert _fails(tb.test_logit_gradient_closed_forms)
+
+
+def test_dropped_rows_sent_back_is_caught(monkeypatch):
+    def wrong_combine(gate_w, recv_slot, o, dy_lat):
+        dy = np.asarray(dy_lat, dtype=np.float64)
+        return (np.einsum("tl,tjl->tj", dy, np.asarray(o, dtype=np.float64)),
+                np.asarray(gate_w, dtype=np.float64)[:, :, None] * dy[:, None, :])
+    monkeypatch.setattr(ob, "combine_backward", wrong_combine)
+    assert _fails(tb.test_dropped_assignments_get_nothing)
