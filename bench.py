@@ -33,8 +33,8 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 kernel names of the stages (substrings that all must match)
 STAGE_KERNEL = {
     "latent": ("dense_bf16_kernel",),
-    "expert_gate_up": ("ragged_gemm_kernel", "true>"),
-    "expert_down": ("ragged_gemm_kernel", "false>"),
+    "expert_gate_up": ("ragged_gemm_kernel", ", 1>"),
+    "expert_down": ("ragged_gemm_kernel", ", 0>"),
     "shared_gate_up": ("swiglu_bf16_kernel",),
     "output": ("dense_bf16_kernel",),
     "combine": ("combine_kernel",),

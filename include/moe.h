@@ -109,6 +109,10 @@ typedef struct {
   int64_t dropless_dispatch_ws_bytes; /* workspace of moe_dispatch_dropless             */
   int64_t dropless_experts_ws_bytes;  /* workspace of moe_experts_dropless              */
   int64_t dropless_forward_ws_bytes;  /* workspace of moe_forward_dropless (taps NULL)  */
+  /* backward of the routed path (moe_*_backward) */
+  int64_t backward_rows;              /* padded expert-major rows the backward works in */
+  int64_t experts_bwd_ws_bytes;       /* workspace of moe_experts_backward              */
+  int64_t backward_ws_bytes;          /* workspace of moe_backward_routed               */
 } moe_plan;
 
 /* Weights of one branch (device pointers, element type = dtype unless noted). */
@@ -342,6 +346,90 @@ moe_status moe_forward_dropless_profiled(const moe_config* cfg, const moe_weight
                                          const void* x, void* y, const moe_dropless_taps* taps,
                                          int64_t* counts, void* ws, size_t ws_bytes, void* stream,
                                          void* const* stage_events, int32_t n_events);
+
+/* ------------------------------------------------------------------------
+ * Backward of the routed path (training).  The pages train this branch
+ * (lamjinlab.com section 2) and print no backward pass; these entry points
+ * are the derivative of the forward above for a fixed routing, one per
+ * forward step, each the transpose of its forward:
+ *   combine   -> d_gates[t][j] = <dy_latent[t], o[t][j]> and the row
+ *                gradient g[t][j] * dy_latent[t] at o's pool slot
+ *   experts   -> per expert, with a = u W_g^T, b = u W_u^T recomputed:
+ *                dh = do W_d, da = dh * b * silu'(a), db = dh * silu(a),
+ *                du = da W_g + db W_u (dgrad), dW_d = do^T (silu(a) * b),
+ *                dW_g = da^T u, dW_u = db^T u (wgrad, summed over the
+ *                expert's rows of every wave)
+ *   dispatch  -> dz[t] = sum over receiver-kept j of du at (t, j)'s slot
+ *   route     -> d_logits through the softmax over the k selected logits
+ * Unselected experts and the balancing bias get no gradient (ranhao.site
+ * section 2.2: the bias is a heuristic outside the gradient); dropped
+ * assignments get nothing (lamjinlab.com section 4).  bf16 activations and
+ * weights with fp32 accumulation; d_gates and d_logits fp32; weight
+ * gradients bf16 in the weights' [out, in] layout, each the full fp32 sum
+ * over the expert's rows rounded once.  bf16 only, d_latent and d_ff
+ * multiples of 256 (else MOE_ERR_UNSUPPORTED).  All pointers device unless
+ * noted.  Buffers, counts and slots are those of the forward call whose
+ * gradient is taken (moe_taps gives them).
+ * ------------------------------------------------------------------------ */
+
+/* Transpose of moe_combine.  dy_latent [T][L]; d_gates (out) [T][k] fp32
+   (0 for a dropped assignment); d_expert_out (out) expert_out_bytes: row
+   gates[t][j] * dy_latent[t] at the (wave, pool, slot) each kept (t, j)
+   read in the forward; other rows are not written. */
+moe_status moe_combine_backward(const moe_config* cfg, const void* expert_out,
+                                const int32_t* topk_idx, const int32_t* pool_slot,
+                                const int32_t* recv_slot, const float* gates,
+                                const void* dy_latent, float* d_gates,
+                                void* d_expert_out, void* stream);
+
+/* Transpose of moe_experts.  pools, bank_rows, expert_count: the forward's;
+   d_expert_out: from moe_combine_backward; d_pool_rows (out)
+   expert_out_bytes: du of every kept row at its (wave, pool, slot), other
+   rows not written; dw_gate, dw_up (out) [E][F][L], dw_down (out) [E][L][F]
+   bf16, written whole (zero for an expert without rows).  ws at least
+   experts_bwd_ws_bytes, 256-byte aligned. */
+moe_status moe_experts_backward(const moe_config* cfg, const void* pools,
+                                const int32_t* bank_rows, const int32_t* expert_count,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                const void* d_expert_out, void* d_pool_rows,
+                                void* dw_gate, void* dw_up, void* dw_down, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Transpose of moe_dispatch: dz (out) [T][L] bf16, dz[t] = the fp32 sum of
+   the d_pool_rows rows of t's receiver-kept assignments, in j order (zero
+   for a token with none). */
+moe_status moe_dispatch_backward(const moe_config* cfg, const int32_t* topk_idx,
+                                 const int32_t* pool_slot, const int32_t* recv_slot,
+                                 const void* d_pool_rows, void* dz, void* stream);
+
+/* Transpose of the gate softmax of moe_route: d_logits (out) [T][E] fp32,
+   d_logits[t][topk_idx[t][j]] = g_j (dg_j - sum_i g_i dg_i), 0 elsewhere.
+   Only T, n_experts and top_k of *cfg are read. */
+moe_status moe_route_backward(const moe_config* cfg, const int32_t* topk_idx,
+                              const float* gates, const float* d_gates,
+                              float* d_logits, void* stream);
+
+/* The four in order: saved (host struct) names the forward's topk_idx,
+   gates, pool_slot, recv_slot, expert_count, bank_rows, pools and
+   expert_out (all required); w supplies w_gate, w_up, w_down.  dz, d_logits,
+   dw_* as above; ws at least backward_ws_bytes, 256-byte aligned. */
+moe_status moe_backward_routed(const moe_config* cfg, const moe_weights* w,
+                               const moe_taps* saved, const void* dy_latent, void* dz,
+                               float* d_logits, void* dw_gate, void* dw_up, void* dw_down,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Stages of moe_backward_routed, in launch order: 0 combine backward,
+   1 padded expert layout and tile lists, 2 row gathers, 3 pre-activation
+   recompute GEMM, 4 dh GEMM with the SwiGLU backward, 5 du GEMM, 6 dW_down,
+   7 dW_gate, 8 dW_up, 9 dispatch backward, 10 route backward. */
+int32_t moe_backward_routed_stage_count(void);
+
+/* moe_backward_routed recording stage_events as moe_forward_profiled does. */
+moe_status moe_backward_routed_profiled(const moe_config* cfg, const moe_weights* w,
+                                        const moe_taps* saved, const void* dy_latent, void* dz,
+                                        float* d_logits, void* dw_gate, void* dw_up,
+                                        void* dw_down, void* ws, size_t ws_bytes, void* stream,
+                                        void* const* stage_events, int32_t n_events);
 
 #ifdef __cplusplus
 }

@@ -1,9 +1,11 @@
-"""Pooled-wave capacity-dispatch MoE branch (forward) for MI355X / gfx950.
+"""Pooled-wave capacity-dispatch MoE branch (forward, and the backward of its
+routed path) for MI355X / gfx950.
 
 Thin torch binding over the C ABI in include/moe.h (libmoe.so).  torch only
 provides device memory and the current stream; every step of the branch runs
 in the HIP kernels of the library.  The same names as the C entry points:
-route, dispatch, experts, combine, forward, plus make_config / plan.
+route, dispatch, experts, combine, forward, their *_backward transposes and
+BackwardRouted (moe_backward_routed), plus make_config / plan.
 """
 from __future__ import annotations
 
@@ -16,7 +18,8 @@ from . import abi
 
 __all__ = ["make_config", "plan", "route", "dispatch", "experts", "combine", "forward",
            "dispatch_dropless", "experts_dropless", "combine_dropless", "forward_dropless",
-           "library", "MoeError"]
+           "combine_backward", "experts_backward", "dispatch_backward", "route_backward",
+           "BackwardRouted", "library", "MoeError"]
 
 MoeError = abi.MoeError
 _DT = {"f32": abi.MOE_F32, "bf16": abi.MOE_BF16, torch.float32: abi.MOE_F32,
@@ -319,3 +322,95 @@ def forward_dropless(cfg, weights: Dict[str, torch.Tensor], x: torch.Tensor, tap
     f = ForwardDropless(cfg, weights, x.device, taps=taps)
     y = f(x)
     return y, f.counts, f.tap_t
+
+
+# ---------------------------------------------------------------- backward
+def combine_backward(cfg, expert_out, topk_idx, pool_slot, recv_slot, gates, dy_latent,
+                     d_gates=None, d_expert_out=None):
+    """(d_gates [T, k] fp32, d_expert_out bytes) = transpose of combine."""
+    p = plan(cfg)
+    dev = dy_latent.device
+    if d_gates is None:
+        d_gates = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    if d_expert_out is None:
+        d_expert_out = torch.empty(p["expert_out_bytes"], dtype=torch.uint8, device=dev)
+    abi.check("moe_combine_backward", library().moe_combine_backward(
+        C.byref(cfg), _ptr(expert_out), _ptr(topk_idx), _ptr(pool_slot), _ptr(recv_slot),
+        _ptr(gates), _ptr(dy_latent), _ptr(d_gates), _ptr(d_expert_out), _stream(dev)))
+    return d_gates, d_expert_out
+
+
+def experts_backward(cfg, pools, bank_rows, expert_count, w_gate, w_up, w_down, d_expert_out,
+                     d_pool_rows=None, dw=None):
+    """(d_pool_rows bytes, (dw_gate, dw_up, dw_down)) = transpose of experts."""
+    p = plan(cfg)
+    dev = pools.device
+    if d_pool_rows is None:
+        d_pool_rows = torch.empty(p["expert_out_bytes"], dtype=torch.uint8, device=dev)
+    if dw is None:
+        dw = (torch.empty_like(w_gate), torch.empty_like(w_up), torch.empty_like(w_down))
+    ws = _ws(p["experts_bwd_ws_bytes"], dev)
+    abi.check("moe_experts_backward", library().moe_experts_backward(
+        C.byref(cfg), _ptr(pools), _ptr(bank_rows), _ptr(expert_count), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(d_expert_out), _ptr(d_pool_rows), _ptr(dw[0]), _ptr(dw[1]),
+        _ptr(dw[2]), _ptr(ws), ws.numel(), _stream(dev)))
+    return d_pool_rows, dw
+
+
+def dispatch_backward(cfg, topk_idx, pool_slot, recv_slot, d_pool_rows, dz=None):
+    """dz [T, L] = transpose of dispatch (sum over a token's kept rows)."""
+    dev = d_pool_rows.device
+    if dz is None:
+        dz = torch.empty((cfg.T, cfg.d_latent), dtype=_tdt(cfg), device=dev)
+    abi.check("moe_dispatch_backward", library().moe_dispatch_backward(
+        C.byref(cfg), _ptr(topk_idx), _ptr(pool_slot), _ptr(recv_slot), _ptr(d_pool_rows),
+        _ptr(dz), _stream(dev)))
+    return dz
+
+
+def route_backward(cfg, topk_idx, gates, d_gates, d_logits=None):
+    """d_logits [T, E] fp32 = transpose of the gate softmax."""
+    dev = gates.device
+    if d_logits is None:
+        d_logits = torch.empty((cfg.T, cfg.n_experts), dtype=torch.float32, device=dev)
+    abi.check("moe_route_backward", library().moe_route_backward(
+        C.byref(cfg), _ptr(topk_idx), _ptr(gates), _ptr(d_gates), _ptr(d_logits), _stream(dev)))
+    return d_logits
+
+
+class BackwardRouted:
+    """Reusable routed-path backward bound to a Forward built with taps=True:
+    its saved routing, pools and expert outputs feed the gradient."""
+
+    def __init__(self, fwd: "Forward"):
+        if fwd.taps is None:
+            raise ValueError("the forward must keep its taps (taps=True)")
+        cfg, dev = fwd.cfg, fwd.y.device
+        self.cfg, self.fwd = cfg, fwd
+        self.p = fwd.p
+        self.ws = _ws(self.p["backward_ws_bytes"], dev)
+        self.dz = torch.empty((cfg.T, cfg.d_latent), dtype=_tdt(cfg), device=dev)
+        self.d_logits = torch.empty((cfg.T, cfg.n_experts), dtype=torch.float32, device=dev)
+        w = fwd.w
+        self.dw = (torch.empty_like(w["w_gate"]), torch.empty_like(w["w_up"]),
+                   torch.empty_like(w["w_down"]))
+
+    def _args(self, dy_latent):
+        return (C.byref(self.cfg), C.byref(self.fwd.wstruct), C.byref(self.fwd.taps),
+                _ptr(dy_latent), _ptr(self.dz), _ptr(self.d_logits), _ptr(self.dw[0]),
+                _ptr(self.dw[1]), _ptr(self.dw[2]), _ptr(self.ws), self.ws.numel(),
+                _stream(dy_latent.device))
+
+    def __call__(self, dy_latent: torch.Tensor):
+        abi.check("moe_backward_routed", library().moe_backward_routed(*self._args(dy_latent)))
+        return self.dz, self.d_logits, self.dw
+
+    def profiled(self, dy_latent: torch.Tensor, events):
+        arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+        abi.check("moe_backward_routed_profiled", library().moe_backward_routed_profiled(
+            *self._args(dy_latent), arr, len(events)))
+        return self.dz, self.d_logits, self.dw
+
+
+def backward_stage_count() -> int:
+    return library().moe_backward_routed_stage_count()

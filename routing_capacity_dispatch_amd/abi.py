@@ -36,7 +36,8 @@ class MoePlan(C.Structure):
         "row_bytes", "pool_block_bytes", "ids_offset", "pools_bytes", "expert_out_bytes",
         "max_expert_rows", "dispatch_ws_bytes", "experts_ws_bytes", "forward_ws_bytes",
         "dropless_rows", "dropless_dispatch_ws_bytes", "dropless_experts_ws_bytes",
-        "dropless_forward_ws_bytes")]
+        "dropless_forward_ws_bytes", "backward_rows", "experts_bwd_ws_bytes",
+        "backward_ws_bytes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -90,12 +91,27 @@ SIGNATURES = {
                                                 _P, _P, C.POINTER(MoeDroplessTaps), _P, _P,
                                                 C.c_size_t, _P, C.POINTER(C.c_void_p),
                                                 C.c_int32]),
+    "moe_combine_backward": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_experts_backward": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, C.c_size_t, _P]),
+    "moe_dispatch_backward": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P]),
+    "moe_route_backward": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P]),
+    "moe_backward_routed": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights),
+                                      C.POINTER(MoeTaps), _P, _P, _P, _P, _P, _P, _P,
+                                      C.c_size_t, _P]),
+    "moe_backward_routed_stage_count": (C.c_int32, []),
+    "moe_backward_routed_profiled": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights),
+                                               C.POINTER(MoeTaps), _P, _P, _P, _P, _P, _P, _P,
+                                               C.c_size_t, _P, C.POINTER(C.c_void_p),
+                                               C.c_int32]),
 }
 
 STAGES = ["latent", "router", "topk", "assign", "scatter", "recv_bin", "expert_rows",
           "expert_gate_up", "expert_down", "combine", "shared_gate_up", "output"]
 DROPLESS_STAGES = ["latent", "router", "topk", "sort", "scatter", "tiles", "expert_gate_up",
                    "expert_down", "combine", "shared_gate_up", "output"]
+BACKWARD_STAGES = ["combine_bwd", "layout", "gather", "recompute", "dh", "du", "dw_down",
+                   "dw_gate", "dw_up", "dispatch_bwd", "route_bwd"]
 
 _lib = None
 

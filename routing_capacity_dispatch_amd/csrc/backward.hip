@@ -1,0 +1,208 @@
+// Backward of the routed path, the parts that move rows and indices: the
+// transpose of combine (gate gradients and the gate-scaled row gradients
+// sent back to the pool slots the forward read), the softmax backward over
+// the k selected logits, and the padded expert-major layout the grouped
+// dgrad / wgrad GEMMs work in (each expert's rows contiguous, rounded up to
+// a whole 64-row K tile with zero rows so that wgrad contracts over them).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// counts[e] = rows expert e kept over all waves; offsets = exclusive scan of
+// counts rounded up to 64 (offsets[E] = the padded total).
+__global__ __launch_bounds__(1024) void bwd_offsets_kernel(const int32_t* __restrict__ expert_count, int E, int W,
+                                                           int cap_recv, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets) {
+  __shared__ int part[16];
+  __shared__ int total;
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E)
+    for (int w = 0; w < W; ++w) c += min(max(expert_count[(int64_t)w * E + e], 0), cap_recv);
+  const int ex = block_excl_scan_1024((c + 63) & ~63, part, &total);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = ex;
+  }
+  if (e == 0) offsets[E] = total;
+}
+
+// Flat pool-row index ((w * P + p) * C_send + slot) of padded row i of the
+// expert-major order (waves in order, receiver slots in order); -1 for the
+// padding rows after an expert's rows.  Counts and slots are clamped to the
+// block, so malformed lists cannot send the GEMMs outside the pools.
+__global__ __launch_bounds__(64) void bwd_gidx_kernel(const int32_t* __restrict__ bank_rows,
+                                                      const int32_t* __restrict__ expert_count,
+                                                      const int32_t* __restrict__ offsets, int E, int P, int W,
+                                                      int cap_send, int cap_recv, int32_t* __restrict__ gidx) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int p = e / (E / P);
+  int off = offsets[e];
+  for (int w = 0; w < W; ++w) {
+    const int c = min(max(expert_count[(int64_t)w * E + e], 0), cap_recv);
+    const int32_t* br = bank_rows + ((int64_t)w * E + e) * cap_recv;
+    const int base = (w * P + p) * cap_send;
+    for (int r = lane; r < c; r += 64) gidx[off + r] = base + min(max(br[r], 0), cap_send - 1);
+    off += c;
+  }
+  for (int r = off + lane; r < offsets[e + 1]; r += 64) gidx[r] = -1;
+}
+
+// dst row i = the pool row gidx[i] (block = i / block_rows at block_bytes
+// apart, rows row_bytes apart inside a block), or zeros where gidx[i] < 0.
+// 16-byte chunks, grid-stride.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src, int block_rows,
+                                                          int64_t block_bytes, int64_t row_bytes,
+                                                          const int32_t* __restrict__ gidx,
+                                                          const int32_t* __restrict__ nrows, char* __restrict__ dst) {
+  const int cpr = (int)(row_bytes / 16);
+  const int64_t total = (int64_t)(*nrows) * cpr;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+    const int64_t i = q / cpr;
+    const int c = (int)(q - i * cpr);
+    const int fi = gidx[i];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (fi >= 0) {
+      const int blk = fi / block_rows;
+      v = ld16(src + blk * block_bytes + (int64_t)(fi - blk * block_rows) * row_bytes + (int64_t)c * 16);
+    }
+    st16(dst + i * row_bytes + (int64_t)c * 16, v);
+  }
+}
+
+// Transpose of combine, one wavefront per token t: for each receiver-kept
+// assignment j, d_gates[t, j] = <dy[t], o[t, j]> (fp32, lane partial sums
+// in chunk order, then a butterfly over the wavefront) and the row
+// g[t, j] * dy[t] goes to the pool slot the forward read o[t, j] from.  A
+// dropped assignment gets d_gates = 0 and no row.
+template <int kMaxChunks>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int k = a.k, epp = a.E / a.P;
+  const int64_t w = t / a.Tw;
+  const int chunks = (int)(a.row_bytes / 16);
+  // dy[t] in registers: chunk c = i * 64 + lane
+  float dy[kMaxChunks][8];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = i * 64 + lane;
+    if (c < chunks) unpack(ld16(static_cast<const char*>(a.dy) + t * a.row_bytes + (int64_t)c * 16), dy[i], bf16_t{});
+  }
+  for (int j = 0; j < k; ++j) {
+    const int64_t q = t * k + j;
+    const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
+    const bool kept = rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send;
+    if (!kept) {
+      if (lane == 0) a.d_gates[q] = 0.0f;
+      continue;
+    }
+    const int64_t row = (w * a.P + e / epp) * a.cap_send + ps;
+    const float g = a.gates[q];
+    const char* o = static_cast<const char*>(a.expert_out) + row * a.row_bytes;
+    char* d = static_cast<char*>(a.d_expert_out) + row * a.row_bytes;
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = i * 64 + lane;
+      if (c >= chunks) continue;
+      float f[8], out[8];
+      unpack(ld16(o + (int64_t)c * 16), f, bf16_t{});
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        s = fmaf(dy[i][x], f[x], s);
+        out[x] = g * dy[i][x];
+      }
+      st16(d + (int64_t)c * 16, pack(out, bf16_t{}));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (lane == 0) a.d_gates[q] = s;
+  }
+}
+
+// Softmax backward over the k selected raw logits, one wavefront per token:
+// d_logits[t, e_j] = g_j (dg_j - sum_i g_i dg_i); every other logit of the
+// token gets 0 (the selection is piecewise constant, the bias only selects).
+__global__ __launch_bounds__(256) void route_bwd_kernel(const int32_t* __restrict__ topk,
+                                                        const float* __restrict__ gates,
+                                                        const float* __restrict__ d_gates, int64_t T, int k, int E,
+                                                        float* __restrict__ d_logits) {
+  __shared__ int sel[4][64];
+  __shared__ float val[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  float g = 0.0f, dg = 0.0f;
+  int e = -1;
+  if (lane < k) {
+    g = gates[t * k + lane];
+    dg = d_gates[t * k + lane];
+    e = topk[t * k + lane];
+  }
+  float s = g * dg;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  sel[wv][lane] = e;
+  val[wv][lane] = g * (dg - s);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int x = lane; x < E; x += 64) {
+    float v = 0.0f;
+    for (int j = 0; j < k; ++j)
+      if (sel[wv][j] == x) v = val[wv][j];
+    d_logits[t * E + x] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_layout(const int32_t* bank_rows, const int32_t* expert_count, int E, int P, int W,
+                             int64_t cap_send, int64_t cap_recv, int32_t* counts, int32_t* offsets, int32_t* gidx,
+                             hipStream_t s) {
+  bwd_offsets_kernel<<<1, 1024, 0, s>>>(expert_count, E, W, (int)cap_recv, counts, offsets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_gidx_kernel<<<E, 64, 0, s>>>(bank_rows, expert_count, offsets, E, P, W, (int)cap_send, (int)cap_recv, gidx);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* src, int block_rows, int64_t block_bytes, int64_t row_bytes,
+                              const int32_t* gidx, const int32_t* nrows, int64_t max_rows, void* dst,
+                              hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  const int64_t chunks = max_rows * (row_bytes / 16);
+  const int64_t want = (chunks + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  gather_rows_kernel<<<blocks, 256, 0, s>>>(static_cast<const char*>(src), block_rows, block_bytes, row_bytes,
+                                            gidx, nrows, static_cast<char*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((a.T + 3) / 4);
+  const int64_t chunks = a.row_bytes / 16;
+  if (chunks <= 64 * 2)
+    combine_bwd_kernel<2><<<blocks, 256, 0, s>>>(a);
+  else if (chunks <= 64 * 6)
+    combine_bwd_kernel<6><<<blocks, 256, 0, s>>>(a);
+  else if (chunks <= 64 * 16)
+    combine_bwd_kernel<16><<<blocks, 256, 0, s>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const int32_t* topk, const float* gates, const float* d_gates, int64_t T, int k, int E,
+                            float* d_logits, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  route_bwd_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(topk, gates, d_gates, T, k, E, d_logits);
+  return hipGetLastError();
+}
+
+}  // namespace moe

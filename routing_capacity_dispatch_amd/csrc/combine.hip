@@ -1,6 +1,8 @@
 // Gate-weighted combine: y_lat[t] = sum over receiver-kept j of
 // g[t,j] * expert_out[row(t,j)], fp32 accumulation in j order, no
-// renormalisation of the gates.  One wavefront per token: its lanes load the
+// renormalisation of the gates.  With gates == NULL every kept row has
+// weight 1: the transpose of dispatch (a token's row gradient summed over
+// the slots it was sent to).  One wavefront per token: its lanes load the
 // token's k assignments at once, then the rows are read two at a time in
 // 16-byte chunks.
 #include "common.h"
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
     if (rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send) {
       row = (w * a.P + e / epp) * a.cap_send + ps;
-      g = a.gates[q];
+      g = a.gates ? a.gates[q] : 1.0f;
     }
   }
   combine_rows<T>(a.expert_out, row, g, k, a.row_bytes, static_cast<char*>(a.y) + t * a.row_bytes);

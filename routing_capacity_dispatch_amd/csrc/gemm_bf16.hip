@@ -220,8 +220,11 @@ __global__ __launch_bounds__(TL::THREADS) void swiglu_bf16_kernel(SwigluBf16 p) 
 // Dropless grouped GEMMs: list entry t = (expert e, n tile, m tile); expert
 // e's rows are rows [offsets[e], offsets[e+1]) of A and of C.  XCD x runs an
 // eighth of the list, contiguous, so an expert's tiles share one L2.
-template <class TL, bool kSwiglu>
+// kMode: 0 down-projection, 1 SwiGLU (gate and up rows interleaved, h out),
+// 2 the SwiGLU's pre-activations a and b out (the backward's recompute).
+template <class TL, int kMode>
 __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) {
+  constexpr bool kSwiglu = kMode >= 1;
   __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
   // the list's length is known only on the device: deal ceil(n / 8)
   // consecutive entries to each XCD (the grid covers the longest list)
@@ -272,6 +275,32 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
   Acc<TL> acc;
   acc.zero();
   mainloop<TL>(a_src, b_src, p.K / TL::BK, lds, acc);
+  if constexpr (kMode == 2) {
+    // a (gate) and b (up) of the tile's BN / 2 features, fp32: the
+    // backward's silu'(a) is steep near its zero, so a keeps full precision
+    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+    constexpr int ld = (TL::BN / 2) * 4 + kStagePad;
+    constexpr int cpr = (TL::BN / 2) * 4 / 16;
+    const int vr = min(TL::BM, rows - m0), vc = min(cpr, (p.F - c0) * 4 / 16);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int mi = 0; mi < TL::MI; ++mi)
+#pragma unroll
+        for (int q = 0; q < TL::NI / 2; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = acc_row<TL>(wm, mi, lane, r);
+            const int col = wn * (TL::WN / 2) + q * 16 + (lane & 15);
+            *reinterpret_cast<float*>(lds + row * ld + col * 4) = acc.v[mi][2 * q + half][r];
+          }
+      __syncthreads();
+      char* C = p.C + (int64_t)(row0 + m0) * p.c_row_bytes + ((int64_t)half * p.F + c0) * 4;
+      copy_rows<TL>(lds, ld, cpr, vr, vc, [&](int r) { return C + (int64_t)r * p.c_row_bytes; });
+      __syncthreads();
+    }
+    return;
+  }
   const int cols = kSwiglu ? p.F : p.N;
   const int tile_cols = kSwiglu ? TL::BN / 2 : TL::BN;
   const int ld = tile_cols * 2 + kStagePad;
@@ -299,13 +328,19 @@ int ragged_down_cols() { return ExpertTile::BN; }
 
 hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
   if (max_entries <= 0) return hipSuccess;
-  ragged_gemm_kernel<ExpertTile, true><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
+  ragged_gemm_kernel<ExpertTile, 1><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
 
 hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
   if (max_entries <= 0) return hipSuccess;
-  ragged_gemm_kernel<ExpertTile, false><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
+  ragged_gemm_kernel<ExpertTile, 0><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_ragged_preact_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
+  if (max_entries <= 0) return hipSuccess;
+  ragged_gemm_kernel<ExpertTile, 2><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
 

@@ -164,5 +164,79 @@ int ragged_gate_up_cols();
 int ragged_down_cols();
 hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
 hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
+// The forward SwiGLU's gate and up pre-activations (no activation), fp32:
+// row i of C gets a at columns [0, F) and b at [F, 2F) (backward recompute).
+hipError_t launch_ragged_preact_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+// Routed-path backward (bf16).  Row moves and indices (backward.hip):
+// counts[e] = rows expert e kept, offsets = the padded expert-major layout
+// (every expert rounded up to 64 rows), gidx[i] = flat pool row of padded
+// row i or -1 for padding.
+hipError_t launch_bwd_layout(const int32_t* bank_rows, const int32_t* expert_count, int E, int P, int W,
+                             int64_t cap_send, int64_t cap_recv, int32_t* counts, int32_t* offsets, int32_t* gidx,
+                             hipStream_t s);
+// dst row i = pool row gidx[i] of src (blocks of block_rows rows) or zeros;
+// *nrows rows (device), at most max_rows.
+hipError_t launch_gather_rows(const void* src, int block_rows, int64_t block_bytes, int64_t row_bytes,
+                              const int32_t* gidx, const int32_t* nrows, int64_t max_rows, void* dst,
+                              hipStream_t s);
+struct CombineBwdArgs {
+  const void* expert_out;  // [W][P][C_send][L]
+  const void* dy;          // [T][L]
+  const int32_t* topk;
+  const int32_t* pool_slot;
+  const int32_t* recv_slot;
+  const float* gates;
+  int64_t T, Tw;
+  int k, E, P;
+  int64_t cap_send, row_bytes;
+  float* d_gates;       // [T][k]
+  void* d_expert_out;   // [W][P][C_send][L], kept rows written
+};
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s);
+hipError_t launch_route_bwd(const int32_t* topk, const float* gates, const float* d_gates, int64_t T, int k, int E,
+                            float* d_logits, hipStream_t s);
+
+// Grouped dgrad / wgrad GEMMs (gemm_bwd.hip) over the padded layout.
+struct BwdDgrad {
+  const char* A;          // padded rows: do (dh) or [da | db] (du)
+  int64_t a_row_bytes;
+  int64_t a_seg_bytes;    // du: byte offset of db inside an A row
+  const int32_t* offsets;  // [E+1] padded
+  const int32_t* counts;   // [E]
+  const int32_t* list;
+  const int32_t* ntiles;
+  const char* W0;         // [E][K][N]: W_d (dh) or W_g (du)
+  const char* W1;         // du: W_u
+  int E, K, N, F;
+  // dh epilogue
+  const char* AB;         // fp32 pre-activations [a | b], ab_row_bytes apart
+  int64_t ab_row_bytes;
+  char* DADB;             // [da | db]
+  int64_t dadb_row_bytes;
+  char* H;
+  int64_t h_row_bytes;
+  // du epilogue: row i -> C + c_index[i] * c_row_bytes
+  char* C;
+  int64_t c_row_bytes;
+  const int32_t* c_index;
+};
+struct BwdWgrad {
+  const char* X;          // K-major rows of the M operand
+  int64_t x_row_bytes, x_col_bytes;
+  const char* Y;          // K-major rows of the N operand
+  int64_t y_row_bytes, y_col_bytes;
+  const int32_t* offsets;  // [E+1] padded: expert e contracts rows [offsets[e], offsets[e+1])
+  int E, M, N;
+  int tiles_m, tiles_n;
+  char* C;                // [E][M][N]
+};
+int bwd_dgrad_rows();
+int bwd_dgrad_cols();
+int bwd_wgrad_tile();
+hipError_t launch_bwd_dh(const BwdDgrad& p, int64_t max_entries, hipStream_t s);
+hipError_t launch_bwd_du(const BwdDgrad& p, int64_t max_entries, hipStream_t s);
+hipError_t launch_bwd_wgrad(const BwdWgrad& p, hipStream_t s);
 
 }  // namespace moe

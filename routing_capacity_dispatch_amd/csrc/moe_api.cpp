@@ -85,6 +85,15 @@ void capped_entries(const moe_config* c, int64_t max_rows, int64_t* ent0, int64_
   *ent1 = mt * ceil_div(c->d_latent, moe::ragged_down_cols());
 }
 
+// Tile-list bounds of the backward's grouped dgrad GEMMs over R padded
+// rows: sum_e ceil(rows_e / bm) <= R / bm + E M tiles.
+void backward_entries(const moe_config* c, int64_t R, int64_t* pre, int64_t* dh, int64_t* du) {
+  const int64_t mt = ceil_div(R, moe::bwd_dgrad_rows()) + c->n_experts;
+  *pre = mt * ceil_div(c->d_ff, moe::ragged_gate_up_cols());
+  *dh = mt * ceil_div(c->d_ff, moe::bwd_dgrad_cols());
+  *du = mt * ceil_div(c->d_latent, moe::bwd_dgrad_cols());
+}
+
 moe_status plan_impl(const moe_config* c, moe_plan* p) {
   if (!c || !p) return MOE_ERR_INVALID_ARG;
   moe_status st = check_route_shape(c);
@@ -213,6 +222,34 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   df.take(p->dropless_dispatch_ws_bytes);
   df.take(p->dropless_experts_ws_bytes);
   p->dropless_forward_ws_bytes = df.used;
+
+  // backward of the routed path: expert e's kept rows, rounded up to 64
+  const int64_t kept_max = T * k < E * W * cr ? T * k : E * W * cr;
+  const int64_t R = kept_max + 63 * E;
+  int64_t bpre, bdh, bdu;
+  backward_entries(c, R, &bpre, &bdh, &bdu);
+  if (R > kI32Max || bpre > kI32Max / 3 || bdh > kI32Max / 3 || bdu > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+  p->backward_rows = R;
+  Carver bx{nullptr, 0};
+  bx.take(E * 4);           // rows per expert
+  bx.take((E + 1) * 4);     // padded offsets
+  bx.take(R * 4);           // pool row of each padded row
+  bx.take(bpre * 12);       // recompute tile list
+  bx.take(bdh * 12);        // dh tile list
+  bx.take(bdu * 12);        // du tile list
+  bx.take(16);              // list lengths
+  bx.take(R * L * 2);       // u rows
+  bx.take(R * L * 2);       // do rows
+  bx.take(R * 2 * F * 4);   // pre-activations a | b (fp32)
+  bx.take(R * 2 * F * 2);   // da | db
+  bx.take(R * F * 2);       // h
+  p->experts_bwd_ws_bytes = bx.used;
+  Carver bb{nullptr, 0};
+  bb.take(T * k * 4);              // d_gates
+  bb.take(p->expert_out_bytes);    // d_expert_out
+  bb.take(p->expert_out_bytes);    // d_pool_rows
+  bb.take(p->experts_bwd_ws_bytes);
+  p->backward_ws_bytes = bb.used;
   return MOE_OK;
 }
 
@@ -810,4 +847,279 @@ MOE_API moe_status moe_forward_dropless_profiled(const moe_config* cfg, const mo
   for (int i = 0; i < n_events; ++i)
     if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
   return forward_dropless_impl(cfg, w, x, y, taps, counts, ws, ws_bytes, stream, stage_events, n_events);
+}
+
+// ------------------------------------------------------------------ backward
+namespace {
+
+constexpr int kBackwardStages = 11;
+
+moe_status check_backward(const moe_config* cfg, moe_plan* p) {
+  moe_status st = plan_impl(cfg, p);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16 || cfg->d_latent % 256 || cfg->d_ff % 256) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status run_combine_bwd(const moe_config* c, const moe_plan& p, const void* expert_out, const int32_t* topk,
+                           const int32_t* pool_slot, const int32_t* recv_slot, const float* gates,
+                           const void* dy, float* d_gates, void* d_expert_out, hipStream_t s) {
+  moe::CombineBwdArgs a{};
+  a.expert_out = expert_out;
+  a.dy = dy;
+  a.topk = topk;
+  a.pool_slot = pool_slot;
+  a.recv_slot = recv_slot;
+  a.gates = gates;
+  a.T = c->T;
+  a.Tw = p.tokens_per_wave;
+  a.k = c->top_k;
+  a.E = c->n_experts;
+  a.P = c->n_pools;
+  a.cap_send = p.cap_send;
+  a.row_bytes = p.row_bytes;
+  a.d_gates = d_gates;
+  a.d_expert_out = d_expert_out;
+  return hip_status(moe::launch_combine_bwd(a, s));
+}
+
+moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* pools, const int32_t* bank_rows,
+                           const int32_t* expert_count, const void* wg, const void* wu, const void* wd,
+                           const void* d_expert_out, void* d_pool_rows, void* dwg, void* dwu, void* dwd,
+                           void* ws, hipStream_t s, Marks* m) {
+  const int E = c->n_experts;
+  const int64_t L = c->d_latent, F = c->d_ff, R = p.backward_rows;
+  int64_t epre, edh, edu;
+  backward_entries(c, R, &epre, &edh, &edu);
+  Carver cv{static_cast<char*>(ws), 0};
+  int32_t* counts = static_cast<int32_t*>(cv.take(E * 4));
+  int32_t* offsets = static_cast<int32_t*>(cv.take((int64_t)(E + 1) * 4));
+  int32_t* gidx = static_cast<int32_t*>(cv.take(R * 4));
+  int32_t* list_pre = static_cast<int32_t*>(cv.take(epre * 12));
+  int32_t* list_dh = static_cast<int32_t*>(cv.take(edh * 12));
+  int32_t* list_du = static_cast<int32_t*>(cv.take(edu * 12));
+  int32_t* ntiles = static_cast<int32_t*>(cv.take(16));
+  char* U = static_cast<char*>(cv.take(R * L * 2));
+  char* DO = static_cast<char*>(cv.take(R * L * 2));
+  char* AB = static_cast<char*>(cv.take(R * 2 * F * 4));
+  char* DADB = static_cast<char*>(cv.take(R * 2 * F * 2));
+  char* H = static_cast<char*>(cv.take(R * F * 2));
+  const int bm = moe::bwd_dgrad_rows();
+  hipError_t e = moe::launch_bwd_layout(bank_rows, expert_count, E, c->n_pools, c->n_waves, p.cap_send,
+                                        p.cap_recv, counts, offsets, gidx, s);
+  if (e == hipSuccess)
+    e = moe::launch_ragged_tiles(offsets, E, bm, (int)ceil_div(F, moe::ragged_gate_up_cols()),
+                                 (int)ceil_div(F, moe::bwd_dgrad_cols()), list_pre, list_dh, ntiles, s);
+  if (e == hipSuccess)
+    e = moe::launch_ragged_tiles(offsets, E, bm, (int)ceil_div(L, moe::bwd_dgrad_cols()), 0, list_du, list_du,
+                                 ntiles + 2, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  // u and do rows in the padded expert-major order (zero padding rows)
+  if (e == hipSuccess)
+    e = moe::launch_gather_rows(pools, (int)p.cap_send, p.pool_block_bytes, p.row_bytes, gidx, offsets + E, R, U,
+                                s);
+  if (e == hipSuccess)
+    e = moe::launch_gather_rows(d_expert_out, (int)p.cap_send, p.cap_send * p.row_bytes, p.row_bytes, gidx,
+                                offsets + E, R, DO, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // recompute a = u W_g^T, b = u W_u^T
+  moe::RaggedGemm g{};
+  g.A = U;
+  g.a_row_bytes = L * 2;
+  g.offsets = offsets;
+  g.list = list_pre;
+  g.ntiles = ntiles;
+  g.W0 = static_cast<const char*>(wg);
+  g.W1 = static_cast<const char*>(wu);
+  g.E = E;
+  g.F = (int)F;
+  g.K = (int)L;
+  g.C = AB;
+  g.c_row_bytes = 2 * F * 4;
+  e = moe::launch_ragged_preact_bf16(g, epre, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // dh = do W_d and the SwiGLU backward
+  moe::BwdDgrad d{};
+  d.A = DO;
+  d.a_row_bytes = L * 2;
+  d.offsets = offsets;
+  d.counts = counts;
+  d.list = list_dh;
+  d.ntiles = ntiles + 1;
+  d.W0 = static_cast<const char*>(wd);
+  d.E = E;
+  d.K = (int)L;
+  d.N = (int)F;
+  d.F = (int)F;
+  d.AB = AB;
+  d.ab_row_bytes = 2 * F * 4;
+  d.DADB = DADB;
+  d.dadb_row_bytes = 2 * F * 2;
+  d.H = H;
+  d.h_row_bytes = F * 2;
+  e = moe::launch_bwd_dh(d, edh, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // du = da W_g + db W_u, rows back to their pool slots
+  moe::BwdDgrad u{};
+  u.A = DADB;
+  u.a_row_bytes = 2 * F * 2;
+  u.a_seg_bytes = F * 2;
+  u.offsets = offsets;
+  u.counts = counts;
+  u.list = list_du;
+  u.ntiles = ntiles + 2;
+  u.W0 = static_cast<const char*>(wg);
+  u.W1 = static_cast<const char*>(wu);
+  u.E = E;
+  u.K = (int)F;
+  u.N = (int)L;
+  u.F = (int)F;
+  u.C = static_cast<char*>(d_pool_rows);
+  u.c_row_bytes = p.row_bytes;
+  u.c_index = gidx;
+  e = moe::launch_bwd_du(u, edu, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // weight gradients over each expert's padded rows
+  const int tile = moe::bwd_wgrad_tile();
+  auto wgrad = [&](const char* X, int64_t xr, int64_t xc, const char* Y, int64_t yr, int M, int N, void* C) {
+    moe::BwdWgrad w{};
+    w.X = X;
+    w.x_row_bytes = xr;
+    w.x_col_bytes = xc;
+    w.Y = Y;
+    w.y_row_bytes = yr;
+    w.y_col_bytes = 0;
+    w.offsets = offsets;
+    w.E = E;
+    w.M = M;
+    w.N = N;
+    w.tiles_m = M / tile;
+    w.tiles_n = N / tile;
+    w.C = static_cast<char*>(C);
+    hipError_t r = moe::launch_bwd_wgrad(w, s);
+    if (r == hipSuccess && m) r = m->mark(s);
+    return r;
+  };
+  e = wgrad(DO, L * 2, 0, H, F * 2, (int)L, (int)F, dwd);
+  if (e == hipSuccess) e = wgrad(DADB, 2 * F * 2, 0, U, L * 2, (int)F, (int)L, dwg);
+  if (e == hipSuccess) e = wgrad(DADB, 2 * F * 2, F * 2, U, L * 2, (int)F, (int)L, dwu);
+  return hip_status(e);
+}
+
+moe_status run_dispatch_bwd(const moe_config* c, const moe_plan& p, const int32_t* topk, const int32_t* pool_slot,
+                            const int32_t* recv_slot, const void* d_pool_rows, void* dz, hipStream_t s) {
+  return run_combine(c, p, d_pool_rows, topk, pool_slot, recv_slot, nullptr, dz, s);
+}
+
+moe_status backward_impl(const moe_config* cfg, const moe_weights* w, const moe_taps* sv, const void* dy,
+                         void* dz, float* d_logits, void* dwg, void* dwu, void* dwd, void* ws, size_t ws_bytes,
+                         void* stream, void* const* events, int n_events) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!w || !sv || !w->w_gate || !w->w_up || !w->w_down || !dwg || !dwu || !dwd || !sv->expert_count ||
+      !sv->bank_rows || !sv->pools || !sv->expert_out)
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!sv->topk_idx || !sv->gates || !sv->pool_slot || !sv->recv_slot || !dy || !dz || !d_logits))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.backward_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Marks marks{events, n_events, 0};
+  Marks* m = events ? &marks : nullptr;
+  Carver cv{static_cast<char*>(ws), 0};
+  const int64_t T = cfg->T, k = cfg->top_k;
+  float* d_gates = static_cast<float*>(cv.take(T * k * 4));
+  void* d_expert_out = cv.take(p.expert_out_bytes);
+  void* d_pool_rows = cv.take(p.expert_out_bytes);
+  void* ews = cv.take(p.experts_bwd_ws_bytes);
+  hipError_t e = m ? m->mark(s) : hipSuccess;
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  st = run_combine_bwd(cfg, p, sv->expert_out, sv->topk_idx, sv->pool_slot, sv->recv_slot, sv->gates, dy, d_gates,
+                       d_expert_out, s);
+  if (st == MOE_OK && m) st = hip_status(m->mark(s));
+  if (st == MOE_OK)
+    st = run_experts_bwd(cfg, p, sv->pools, sv->bank_rows, sv->expert_count, w->w_gate, w->w_up, w->w_down,
+                         d_expert_out, d_pool_rows, dwg, dwu, dwd, ews, s, m);
+  if (st == MOE_OK)
+    st = run_dispatch_bwd(cfg, p, sv->topk_idx, sv->pool_slot, sv->recv_slot, d_pool_rows, dz, s);
+  if (st == MOE_OK && m) st = hip_status(m->mark(s));
+  if (st == MOE_OK)
+    st = hip_status(moe::launch_route_bwd(sv->topk_idx, sv->gates, d_gates, T, (int)k, cfg->n_experts, d_logits, s));
+  if (st == MOE_OK && m) st = hip_status(m->mark(s));
+  return st;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_combine_backward(const moe_config* cfg, const void* expert_out, const int32_t* topk_idx,
+                                        const int32_t* pool_slot, const int32_t* recv_slot, const float* gates,
+                                        const void* dy_latent, float* d_gates, void* d_expert_out, void* stream) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!expert_out || !topk_idx || !pool_slot || !recv_slot || !gates || !dy_latent || !d_gates ||
+                     !d_expert_out))
+    return MOE_ERR_INVALID_ARG;
+  return run_combine_bwd(cfg, p, expert_out, topk_idx, pool_slot, recv_slot, gates, dy_latent, d_gates,
+                         d_expert_out, static_cast<hipStream_t>(stream));
+}
+
+MOE_API moe_status moe_experts_backward(const moe_config* cfg, const void* pools, const int32_t* bank_rows,
+                                        const int32_t* expert_count, const void* w_gate, const void* w_up,
+                                        const void* w_down, const void* d_expert_out, void* d_pool_rows,
+                                        void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!expert_count || !bank_rows || !pools || !d_expert_out || !d_pool_rows || !w_gate || !w_up || !w_down ||
+      !dw_gate || !dw_up || !dw_down)
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.experts_bwd_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+  return run_experts_bwd(cfg, p, pools, bank_rows, expert_count, w_gate, w_up, w_down, d_expert_out, d_pool_rows,
+                         dw_gate, dw_up, dw_down, ws, static_cast<hipStream_t>(stream), nullptr);
+}
+
+MOE_API moe_status moe_dispatch_backward(const moe_config* cfg, const int32_t* topk_idx, const int32_t* pool_slot,
+                                         const int32_t* recv_slot, const void* d_pool_rows, void* dz,
+                                         void* stream) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!topk_idx || !pool_slot || !recv_slot || !d_pool_rows || !dz)) return MOE_ERR_INVALID_ARG;
+  return run_dispatch_bwd(cfg, p, topk_idx, pool_slot, recv_slot, d_pool_rows, dz,
+                          static_cast<hipStream_t>(stream));
+}
+
+MOE_API moe_status moe_route_backward(const moe_config* cfg, const int32_t* topk_idx, const float* gates,
+                                      const float* d_gates, float* d_logits, void* stream) {
+  moe_status st = check_route_shape(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!topk_idx || !gates || !d_gates || !d_logits)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_route_bwd(topk_idx, gates, d_gates, cfg->T, cfg->top_k, cfg->n_experts, d_logits,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_backward_routed(const moe_config* cfg, const moe_weights* w, const moe_taps* saved,
+                                       const void* dy_latent, void* dz, float* d_logits, void* dw_gate,
+                                       void* dw_up, void* dw_down, void* ws, size_t ws_bytes, void* stream) {
+  return backward_impl(cfg, w, saved, dy_latent, dz, d_logits, dw_gate, dw_up, dw_down, ws, ws_bytes, stream,
+                       nullptr, 0);
+}
+
+MOE_API int32_t moe_backward_routed_stage_count(void) { return kBackwardStages; }
+
+MOE_API moe_status moe_backward_routed_profiled(const moe_config* cfg, const moe_weights* w, const moe_taps* saved,
+                                                const void* dy_latent, void* dz, float* d_logits, void* dw_gate,
+                                                void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                                void* stream, void* const* stage_events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && !stage_events)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+  return backward_impl(cfg, w, saved, dy_latent, dz, d_logits, dw_gate, dw_up, dw_down, ws, ws_bytes, stream,
+                       stage_events, n_events);
 }

@@ -101,7 +101,7 @@ def workload(name: str, **overrides) -> Workload:
 _TID = dict(x=1, w_latent=2, w_router=3, router_bias=4, w_gate=5, w_up=6,
             w_down=7, w_up_proj=8, ws_gate=9, ws_up=10, ws_down=11,
             zipf_perm=12, share_rows=13, share_counts=14, share_perm=15,
-            share_logits=16)
+            share_logits=16, dy_latent=17)
 
 
 def _seed(seed: int, tid: int, sub: int = 0) -> int:
@@ -176,6 +176,12 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu",
     if with_experts:
         out.update(expert_weights(w, seed, device))
     return out
+
+
+def grad_latent(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
+    """dL/dy_latent [T, L] for the routed-path backward: N(0, 1) rows in the
+    workload's dtype (a stand-in for the gradient a training step brings)."""
+    return normal((w.T, w.d_latent), seed, _TID["dy_latent"], device, 1.0, w.dtype)
 
 
 def expert_weights(w: Workload, seed: int, device="cpu"):

@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header():
     # sizes implied by the header's field lists (natural alignment, no packing)
     assert C.sizeof(abi.MoeConfig) == 8 + 13 * 4 + 4 + 2 * 8 + 2 * 4
-    assert C.sizeof(abi.MoePlan) == 18 * 8
+    assert C.sizeof(abi.MoePlan) == 21 * 8
     assert C.sizeof(abi.MoeWeights) == 10 * 8
     assert C.sizeof(abi.MoeTaps) == 12 * 8
 
@@ -212,3 +212,45 @@ def test_bf16_operands_above_4gib_unsupported(lib):
     ok = rcd.make_config(65536, 6144, 3072, 384, 64, 8, 3072, n_shared=2, d_ff_shared=3072,
                          dtype="bf16")
     assert rcd.plan(ok)["pools_bytes"] < 2 ** 32
+
+
+def test_backward_plan_and_validation(lib):
+    w = synth.workload("marin_16k")
+    p = rcd.plan(rcd.config_of(w))
+    kept_max = min(w.T * w.top_k, w.n_experts * w.n_waves * p["cap_recv"])
+    assert p["backward_rows"] == kept_max + 63 * w.n_experts
+    # u, do, a|b, da|db and h rows dominate the experts' backward workspace
+    R, L, F = p["backward_rows"], w.d_latent, w.d_ff
+    assert p["experts_bwd_ws_bytes"] >= R * (2 * L + 7 * F) * 2
+    assert p["backward_ws_bytes"] >= p["experts_bwd_ws_bytes"] + 2 * p["expert_out_bytes"]
+    for k in ("experts_bwd_ws_bytes", "backward_ws_bytes"):
+        assert p[k] % 256 == 0
+    nul = None
+    fake = C.c_void_p(0x100000)
+    # fp32, or widths not multiples of 256: unsupported
+    f32 = rcd.config_of(synth.workload("tiny_fp32"))
+    assert lib.moe_combine_backward(C.byref(f32), *([fake] * 8), nul) == abi.MOE_ERR_UNSUPPORTED
+    odd = rcd.make_config(64, 256, 192, 16, 4, 2, 256, dtype="bf16")
+    assert lib.moe_dispatch_backward(C.byref(odd), *([fake] * 5), nul) == abi.MOE_ERR_UNSUPPORTED
+    bf = rcd.config_of(synth.workload("mid_bf16"))
+    pb = rcd.plan(bf)
+    assert lib.moe_combine_backward(C.byref(bf), *([fake] * 7), nul, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_backward(C.byref(bf), fake, fake, fake, nul, fake, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(C.byref(bf), fake, fake, nul, fake, nul) == abi.MOE_ERR_INVALID_ARG
+    args = [fake] * 11
+    assert lib.moe_experts_backward(C.byref(bf), *args, fake, pb["experts_bwd_ws_bytes"] - 256,
+                                    nul) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_experts_backward(C.byref(bf), *args, C.c_void_p(0x100010), pb["experts_bwd_ws_bytes"],
+                                    nul) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_experts_backward(C.byref(bf), nul, *args[1:], fake, 1 << 40, nul) == abi.MOE_ERR_INVALID_ARG
+    ww = abi.MoeWeights(*([0x100000] * 10))
+    taps = abi.MoeTaps(*([0x100000] * 12))
+    assert lib.moe_backward_routed(C.byref(bf), C.byref(ww), C.byref(taps), *([fake] * 6), fake,
+                                   pb["backward_ws_bytes"] - 1, nul) == abi.MOE_ERR_WORKSPACE
+    taps.expert_out = None
+    assert lib.moe_backward_routed(C.byref(bf), C.byref(ww), C.byref(taps), *([fake] * 6), fake,
+                                   pb["backward_ws_bytes"], nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_backward_routed(C.byref(bf), C.byref(ww), nul, *([fake] * 6), fake,
+                                   pb["backward_ws_bytes"], nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_backward_routed_stage_count() == len(abi.BACKWARD_STAGES)
+
