@@ -6,7 +6,10 @@
 A step is one moe_forward call (latent projection, router, top-k, pooled
 dispatch with both caps, receiver binning, grouped SwiGLU experts, combine,
 up-projection and shared experts) over one batch of seeded synthetic inputs
-already resident in HBM.  Prints one JSON line.
+already resident in HBM.  Prints one JSON line.  --dropless times the
+dropless ragged variant; --backward times the routed path's backward
+(moe_backward_routed: gate, row and weight gradients for one forward call's
+routing, a seeded dL/dy_latent, forward state resident).
 
 Stage durations come from HIP events the library records between its kernel
 launches on the stream it launches them on (moe_forward_profiled), averaged
@@ -27,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; % bf16 MFMA peak; drop fraction"
+METRIC_BWD = "MoE routed-path bwd tokens/sec on 1 MI355X; % bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 
@@ -39,11 +43,16 @@ STAGE_KERNEL = {
     "output": ("dense_bf16_kernel",),
     "combine": ("combine_kernel",),
     "scatter": ("scatter_kernel",),
+    "recompute": ("ragged_gemm_kernel", ", 2>"),
+    "dh": ("dgrad_kernel", "<0>"),
+    "du": ("dgrad_kernel", "<1>"),
+    "dw_down": ("wgrad_kernel",),
 }
 COPY_KERNEL = ("copyBuffer",)
 # sources of the GEMM kernels: a measured traffic figure is used only while
 # they are unchanged
-KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "dispatch.hip"]
+KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "dispatch.hip",
+                  "gemm_kmajor.h", "gemm_bwd.hip", "backward.hip"]
 
 
 def kernel_source_hash():
@@ -94,11 +103,26 @@ def summarize_pmc(fetch_csv, write_csv, stage, workload, copy_bytes, out_path, c
     print(json.dumps(rec))
 
 
-def stage_work(w, kept, sent, dropless=False):
+def stage_work(w, kept, sent, dropless=False, backward=False):
     """Algorithmic flops (MFMA stages) or bytes (HBM stages) per launch."""
     eb = 2 if w.dtype == "bf16" else 4
     T, D, L, E, k, F = w.T, w.d_model, w.d_latent, w.n_experts, w.top_k, w.d_ff
     S, Fs = w.n_shared, w.d_ff_shared
+    if backward:
+        # kept rows only, never the 64-row padding of the expert layout
+        return {
+            "combine_bwd": ("hbm", T * L * eb + 2 * kept * L * eb + 4 * T * k * 4),
+            "layout": ("hbm", 0.0),
+            "gather": ("hbm", 4 * kept * L * eb),
+            "recompute": ("mfma", 2.0 * kept * L * 2 * F),
+            "dh": ("mfma", 2.0 * kept * L * F),
+            "du": ("mfma", 2.0 * kept * 2 * F * L),
+            "dw_down": ("mfma", 2.0 * kept * L * F),
+            "dw_gate": ("mfma", 2.0 * kept * F * L),
+            "dw_up": ("mfma", 2.0 * kept * F * L),
+            "dispatch_bwd": ("hbm", kept * L * eb + T * L * eb + 3 * T * k * 4),
+            "route_bwd": ("hbm", 3 * T * k * 4 + T * E * 4),
+        }
     if dropless:
         n = kept   # every valid assignment has a row
         return {
@@ -130,7 +154,7 @@ def stage_work(w, kept, sent, dropless=False):
     }
 
 
-def cpu_baseline(w, inp, n_tok, dropless=False):
+def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
     """The fp64 oracle on the first n_tok tokens (its own batch: caps are
     derived for n_tok tokens), weights given as the run's bf16 values."""
     import numpy as np
@@ -155,19 +179,34 @@ def cpu_baseline(w, inp, n_tok, dropless=False):
     wt["expert_weights"] = lambda e: (host["w_gate"][e].to(torch.float64).numpy(),
                                       host["w_up"][e].to(torch.float64).numpy(),
                                       host["w_down"][e].to(torch.float64).numpy())
-    t0 = time.perf_counter()
-    if dropless:
-        r = oracle.forward_dropless(x, wt, top_k=w.top_k)
-    else:
+    if backward:
+        # the saved state of the sample's own forward is not timed
         r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
                            send_cap=w.send_cap, recv_cap=w.recv_cap)
-    dt = time.perf_counter() - t0
-    assert r["y"].shape == (n_tok, w.d_model)
+        dy = f64(dy_latent[:n_tok])
+        t0 = time.perf_counter()
+        g = oracle.routed_backward(r["z"], r["topk_idx"], r["gates"], r["assignment"]["recv_slot"],
+                                   wt["expert_weights"], dy, w.n_experts, o=r["expert_out"],
+                                   experts=())
+        dt = time.perf_counter() - t0
+        assert g["dz"].shape == (n_tok, w.d_latent)
+        what = (f"routed-path backward (dz, d_logits and every present expert's weight "
+                f"gradients, computed and discarded) of the first {n_tok} tokens of the {w.name} "
+                f"inputs as their own batch (caps for {n_tok} tokens)")
+    else:
+        t0 = time.perf_counter()
+        if dropless:
+            r = oracle.forward_dropless(x, wt, top_k=w.top_k)
+        else:
+            r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
+                               send_cap=w.send_cap, recv_cap=w.recv_cap)
+        dt = time.perf_counter() - t0
+        assert r["y"].shape == (n_tok, w.d_model)
+        what = (f"first {n_tok} tokens of the {w.name} inputs as their own batch "
+                f"({'no caps' if dropless else f'caps for {n_tok} tokens'})")
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": blas_threads or cores,
             "kind": "oracle",
-            "sample": f"first {n_tok} tokens of the {w.name} inputs as their own batch "
-                      f"({'no caps' if dropless else f'caps for {n_tok} tokens'}), fp64 numpy, "
-                      f"{dt:.1f} s wall, {cores} cores in the affinity mask"}
+            "sample": f"{what}, fp64 numpy, {dt:.1f} s wall, {cores} cores in the affinity mask"}
 
 
 def main():
@@ -179,7 +218,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--dropless", action="store_true",
                     help="time the dropless ragged variant (moe_forward_dropless) instead")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the routed path's backward (moe_backward_routed) instead")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="oracle sample for the CPU baseline (default 256; 64 with --backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
                     help="measured HBM bytes per launch of the dominant kernel (JSON; default "
@@ -193,7 +235,11 @@ def main():
     ap.add_argument("--stage", default="expert_gate_up", help="stage for --summarize-pmc")
     ap.add_argument("--pmc-command", default="", help="command recorded by --summarize-pmc")
     args = ap.parse_args()
-    run_name = args.workload + ("_dropless" if args.dropless else "")
+    if args.dropless and args.backward:
+        raise SystemExit("--backward times the capped path's backward; drop --dropless")
+    run_name = args.workload + ("_dropless" if args.dropless else "") + ("_backward" if args.backward else "")
+    if args.cpu_tokens is None:
+        args.cpu_tokens = 64 if args.backward else 256
     if args.traffic is None:
         args.traffic = os.path.join(ROOT, "profiles", f"traffic_{run_name}.json")
     if args.summarize_pmc:
@@ -222,14 +268,25 @@ def main():
     inp = synth.make_inputs(w, args.seed, device=dev)
     x = inp["x"]
     weights = {k: v for k, v in inp.items() if k != "x"}
+    dy = None
     if args.dropless:
         fwd = rcd.ForwardDropless(cfg, weights, dev)
         nst = rcd.dropless_stage_count()
         stages = rcd.abi.DROPLESS_STAGES
+        step = fwd
+    elif args.backward:
+        fwd = rcd.Forward(cfg, weights, dev, taps=True)
+        fwd(x)           # the forward call whose gradient is taken: state saved
+        dy = synth.grad_latent(w, args.seed, device=dev)
+        step = rcd.BackwardRouted(fwd)
+        nst = rcd.backward_stage_count()
+        stages = rcd.abi.BACKWARD_STAGES
     else:
         fwd = rcd.Forward(cfg, weights, dev)
         nst = rcd.stage_count()
         stages = rcd.abi.STAGES
+        step = fwd
+    arg = dy if args.backward else x
     if args.calib_copy_mb:
         n = args.calib_copy_mb * 1024 * 1024
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -241,7 +298,7 @@ def main():
 
     print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        fwd(x)
+        step(arg)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -256,7 +313,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(K):
-        fwd.profiled(x, ev[i])
+        step.profiled(arg, ev[i])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -268,7 +325,7 @@ def main():
             per[s] += ev[i][j].elapsed_time(ev[i][j + 1]) / K
     kept, sd, rd = [int(v) for v in fwd.counts.cpu().tolist()]
     sent = kept + rd
-    work = stage_work(w, kept, sent, dropless=args.dropless)
+    work = stage_work(w, kept, sent, dropless=args.dropless, backward=args.backward)
     peak_f = PEAK_TFLOPS[w.dtype]
     st_out = {}
     for s in stages:
@@ -306,7 +363,7 @@ def main():
     gemm_ms = sum(per[s] for s in stages if work[s][0] == "mfma")
     tokens_s = w.T / (ms_step * 1e-3)
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC,
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -318,7 +375,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": run_name, "T": w.T, "d_model": w.d_model, "d_latent": w.d_latent,
+        "config": {"workload": run_name, "pass": "backward" if args.backward else "forward", "T": w.T, "d_model": w.d_model, "d_latent": w.d_latent,
                    "n_experts": w.n_experts, "n_pools": w.n_pools, "top_k": w.top_k,
                    "d_ff": w.d_ff, "n_shared": w.n_shared, "d_ff_shared": w.d_ff_shared,
                    "n_waves": w.n_waves, "caps": [list(w.send_cap), list(w.recv_cap)],
@@ -332,7 +389,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print(f"# cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, dropless=args.dropless)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, dropless=args.dropless,
+                                           backward=args.backward, dy_latent=dy)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

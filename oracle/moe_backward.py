@@ -135,10 +135,9 @@ def experts_backward(z, topk_idx, recv_slot, expert_weights, d_o, experts=None):
     d_o = _f64(d_o)
     du = np.zeros(d_o.shape, dtype=np.float64)
     present = np.unique(topk_idx[keep])
-    wanted = present if experts is None else np.asarray(experts)
+    wanted = set(int(e) for e in (present if experts is None else experts))
     dw = {}
-    for e in np.union1d(present, wanted):
-        e = int(e)
+    for e in sorted(set(int(e) for e in present) | wanted):
         wg, wu, wd = expert_weights(e)
         rows, js = np.nonzero((topk_idx == e) & keep)
         if len(rows) == 0:
@@ -146,9 +145,8 @@ def experts_backward(z, topk_idx, recv_slot, expert_weights, d_o, experts=None):
             continue
         g_u, g_wg, g_wu, g_wd = swiglu_backward(z[rows], wg, wu, wd, d_o[rows, js])
         du[rows, js] = g_u
-        dw[e] = (g_wg, g_wu, g_wd)
-    if experts is not None:
-        dw = {int(e): dw[int(e)] for e in wanted}
+        if e in wanted:   # the others' gradients are computed, not kept
+            dw[e] = (g_wg, g_wu, g_wd)
     return du, dw
 
 
