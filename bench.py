@@ -43,7 +43,7 @@ STAGE_KERNEL = {
     "output": ("dense_bf16_kernel",),
     "combine": ("combine_kernel",),
     "scatter": ("scatter_kernel",),
-    "recompute": ("ragged_gemm_kernel", ", 2>"),
+    "swiglu_bwd": ("ragged_gemm_kernel", ", 2>"),
     "dh": ("dgrad_kernel", "<0>"),
     "du": ("dgrad_kernel", "<1>"),
     "dw_down": ("wgrad_kernel",),
@@ -114,8 +114,8 @@ def stage_work(w, kept, sent, dropless=False, backward=False):
             "combine_bwd": ("hbm", T * L * eb + 2 * kept * L * eb + 4 * T * k * 4),
             "layout": ("hbm", 0.0),
             "gather": ("hbm", 4 * kept * L * eb),
-            "recompute": ("mfma", 2.0 * kept * L * 2 * F),
             "dh": ("mfma", 2.0 * kept * L * F),
+            "swiglu_bwd": ("mfma", 2.0 * kept * L * 2 * F),
             "du": ("mfma", 2.0 * kept * 2 * F * L),
             "dw_down": ("mfma", 2.0 * kept * L * F),
             "dw_gate": ("mfma", 2.0 * kept * F * L),

@@ -419,9 +419,9 @@ moe_status moe_backward_routed(const moe_config* cfg, const moe_weights* w,
                                void* ws, size_t ws_bytes, void* stream);
 
 /* Stages of moe_backward_routed, in launch order: 0 combine backward,
-   1 padded expert layout and tile lists, 2 row gathers, 3 pre-activation
-   recompute GEMM, 4 dh GEMM with the SwiGLU backward, 5 du GEMM, 6 dW_down,
-   7 dW_gate, 8 dW_up, 9 dispatch backward, 10 route backward. */
+   1 padded expert layout and tile lists, 2 row gathers, 3 dh GEMM, 4 gate/up
+   recompute GEMM with the SwiGLU backward, 5 du GEMM, 6 dW_down, 7 dW_gate,
+   8 dW_up, 9 dispatch backward, 10 route backward. */
 int32_t moe_backward_routed_stage_count(void);
 
 /* moe_backward_routed recording stage_events as moe_forward_profiled does. */

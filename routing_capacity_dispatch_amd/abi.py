@@ -110,7 +110,7 @@ STAGES = ["latent", "router", "topk", "assign", "scatter", "recv_bin", "expert_r
           "expert_gate_up", "expert_down", "combine", "shared_gate_up", "output"]
 DROPLESS_STAGES = ["latent", "router", "topk", "sort", "scatter", "tiles", "expert_gate_up",
                    "expert_down", "combine", "shared_gate_up", "output"]
-BACKWARD_STAGES = ["combine_bwd", "layout", "gather", "recompute", "dh", "du", "dw_down",
+BACKWARD_STAGES = ["combine_bwd", "layout", "gather", "dh", "swiglu_bwd", "du", "dw_down",
                    "dw_gate", "dw_up", "dispatch_bwd", "route_bwd"]
 
 _lib = None

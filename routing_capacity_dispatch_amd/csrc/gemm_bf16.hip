@@ -221,7 +221,8 @@ __global__ __launch_bounds__(TL::THREADS) void swiglu_bf16_kernel(SwigluBf16 p) 
 // e's rows are rows [offsets[e], offsets[e+1]) of A and of C.  XCD x runs an
 // eighth of the list, contiguous, so an expert's tiles share one L2.
 // kMode: 0 down-projection, 1 SwiGLU (gate and up rows interleaved, h out),
-// 2 the SwiGLU's pre-activations a and b out (the backward's recompute).
+// 2 the backward's recompute of the gate/up pre-activations with the SwiGLU
+// backward in the epilogue (da, db, h out).
 template <class TL, int kMode>
 __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) {
   constexpr bool kSwiglu = kMode >= 1;
@@ -276,14 +277,58 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
   acc.zero();
   mainloop<TL>(a_src, b_src, p.K / TL::BK, lds, acc);
   if constexpr (kMode == 2) {
-    // a (gate) and b (up) of the tile's BN / 2 features, fp32: the
-    // backward's silu'(a) is steep near its zero, so a keeps full precision
+    static_assert(((TL::BM * ((TL::BN / 2) * 2 + kStagePad) + 1023) & ~1023) + TL::BM * ((TL::BN / 2) * 2 + kStagePad) <=
+                      lds_bytes<TL>(),
+                  "output staging and the dh tile fit the kernel's LDS");
+    // SwiGLU backward at (row, feature) from the fp32 a (gate) and b (up)
+    // of this tile and dh (bf16, rows of p.dH): da = dh b silu'(a),
+    // db = dh silu(a), h = silu(a) b.  da is staged first; db and h wait
+    // packed in the gate accumulator.  Rows past the expert's rows are not
+    // read or written.
     const int wm = wave / TL::WGN, wn = wave % TL::WGN;
-    constexpr int ld = (TL::BN / 2) * 4 + kStagePad;
-    constexpr int cpr = (TL::BN / 2) * 4 / 16;
-    const int vr = min(TL::BM, rows - m0), vc = min(cpr, (p.F - c0) * 4 / 16);
+    constexpr int ld = (TL::BN / 2) * 2 + kStagePad;
+    constexpr int cpr = (TL::BN / 2) * 2 / 16;
+    const int vr = min(TL::BM, rows - m0), vc = min(cpr, (p.F - c0) * 2 / 16);
+    // the tile's dh rows, staged through LDS with coalesced 16-byte loads
+    // (zeros outside the expert's rows), after the staging area of the outputs
+    char* ldh = lds + ((TL::BM * ld + 1023) & ~1023);
+    {
+      const char* DH = p.dH + (int64_t)(row0 + m0) * p.dh_row_bytes + (int64_t)c0 * 2;
+      for (int q = threadIdx.x; q < TL::BM * cpr; q += TL::THREADS) {
+        const int r = q / cpr, c = q - r * cpr;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < vr && c < vc) v = ld16(DH + (int64_t)r * p.dh_row_bytes + c * 16);
+        st16(ldh + r * ld + c * 16, v);
+      }
+    }
+    __syncthreads();
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int mi = 0; mi < TL::MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < TL::NI / 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = acc_row<TL>(wm, mi, lane, r);
+          const int col = wn * (TL::WN / 2) + q * 16 + (lane & 15);
+          float da = 0.0f, db = 0.0f, h = 0.0f;
+          if (m0 + row < rows && c0 + col < p.F) {
+            const float a = acc.v[mi][2 * q][r], b = acc.v[mi][2 * q + 1][r];
+            const float dh = bf16_to_f32(*reinterpret_cast<const uint16_t*>(ldh + row * ld + col * 2));
+            const float sg = 1.0f / (1.0f + __expf(-a));
+            const float sa = a * sg;
+            da = dh * b * sg * (1.0f + a * (1.0f - sg));
+            db = dh * sa;
+            h = sa * b;
+          }
+          *reinterpret_cast<uint16_t*>(lds + row * ld + col * 2) = f32_to_bf16(da);
+          acc.v[mi][2 * q][r] = __uint_as_float((uint32_t)f32_to_bf16(db) | ((uint32_t)f32_to_bf16(h) << 16));
+        }
+    __syncthreads();
+    char* DA = p.C + (int64_t)(row0 + m0) * p.c_row_bytes + (int64_t)c0 * 2;
+    copy_rows<TL>(lds, ld, cpr, vr, vc, [&](int r) { return DA + (int64_t)r * p.c_row_bytes; });
+#pragma unroll
+    for (int pass = 1; pass <= 2; ++pass) {
+      __syncthreads();
 #pragma unroll
       for (int mi = 0; mi < TL::MI; ++mi)
 #pragma unroll
@@ -292,12 +337,13 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
           for (int r = 0; r < 4; ++r) {
             const int row = acc_row<TL>(wm, mi, lane, r);
             const int col = wn * (TL::WN / 2) + q * 16 + (lane & 15);
-            *reinterpret_cast<float*>(lds + row * ld + col * 4) = acc.v[mi][2 * q + half][r];
+            *reinterpret_cast<uint16_t*>(lds + row * ld + col * 2) =
+                static_cast<uint16_t>(__float_as_uint(acc.v[mi][2 * q][r]) >> (pass == 1 ? 0 : 16));
           }
       __syncthreads();
-      char* C = p.C + (int64_t)(row0 + m0) * p.c_row_bytes + ((int64_t)half * p.F + c0) * 4;
-      copy_rows<TL>(lds, ld, cpr, vr, vc, [&](int r) { return C + (int64_t)r * p.c_row_bytes; });
-      __syncthreads();
+      char* dst = pass == 1 ? DA + (int64_t)p.F * 2 : p.H + (int64_t)(row0 + m0) * p.h_row_bytes + (int64_t)c0 * 2;
+      const int64_t rb = pass == 1 ? p.c_row_bytes : p.h_row_bytes;
+      copy_rows<TL>(lds, ld, cpr, vr, vc, [&](int r) { return dst + (int64_t)r * rb; });
     }
     return;
   }
@@ -338,7 +384,7 @@ hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hip
   return hipGetLastError();
 }
 
-hipError_t launch_ragged_preact_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
+hipError_t launch_ragged_swiglu_bwd_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
   if (max_entries <= 0) return hipSuccess;
   ragged_gemm_kernel<ExpertTile, 2><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
   return hipGetLastError();

@@ -2,10 +2,10 @@
 // accumulation, over the padded expert-major row order (expert e's rows at
 // [offsets[e], offsets[e] + counts[e]), zero rows up to offsets[e+1]).
 //
-//   dgrad, dh:  dh[r, :] = do[r, :] W_d[e]       (W_d [L][F] read K-major)
-//               epilogue: the SwiGLU backward at (r, f) from the recomputed
-//               fp32 pre-activations a = u W_g^T, b = u W_u^T:
-//               da = dh b silu'(a), db = dh silu(a), h = silu(a) b
+//   dgrad, dh:  dh[r, :] = do[r, :] W_d[e]       (W_d [L][F] read K-major),
+//               bf16 out; the SwiGLU backward da = dh b silu'(a),
+//               db = dh silu(a), h = silu(a) b then runs in the epilogue of
+//               the forward gate/up GEMM recomputing a and b (gemm_bf16.hip)
 //   dgrad, du:  du[r, :] = da[r, :] W_g[e] + db[r, :] W_u[e]  (two K
 //               segments, W_g / W_u [F][L] read K-major); rows scattered to
 //               the pool slots they came from
@@ -78,7 +78,7 @@ __device__ __forceinline__ void stage(const Acc<TL>& acc, char* lds, int ld, int
 }
 
 // ------------------------------------------------------------------ dgrad
-template <int kMode>  // 0: dh + SwiGLU backward; 1: du (two segments, scattered)
+template <int kMode>  // 0: dh, rows in order; 1: du (two segments, rows scattered)
 __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
   using TL = DgradTile;
   __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
@@ -118,47 +118,11 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
   constexpr int ld = TL::BN * 2 + kStagePad;
   constexpr int cpr = TL::BN * 2 / 16;
   if constexpr (kMode == 0) {
-    // SwiGLU backward: da staged now; db and h kept packed in the
-    // accumulators for the next two passes.  Padding rows get zeros.
-    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
-    const char* AB = p.AB + (int64_t)row0 * p.ab_row_bytes;
-#pragma unroll
-    for (int mi = 0; mi < TL::MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < TL::NI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = acc_row<TL>(wm, mi, lane, r), col = acc_col<TL>(wn, ni, lane);
-          const int gr = m0 + row, f = n0 + col;
-          float da = 0.0f, db = 0.0f, h = 0.0f;
-          if (gr < rows) {
-            const char* ab = AB + (int64_t)gr * p.ab_row_bytes;
-            const float a = *reinterpret_cast<const float*>(ab + (int64_t)f * 4);
-            const float b = *reinterpret_cast<const float*>(ab + ((int64_t)p.F + f) * 4);
-            const float dh = acc.v[mi][ni][r];
-            const float s = 1.0f / (1.0f + __expf(-a));
-            const float sa = a * s;
-            da = dh * b * s * (1.0f + a * (1.0f - s));
-            db = dh * sa;
-            h = sa * b;
-          }
-          *reinterpret_cast<uint16_t*>(lds + row * ld + col * 2) = f32_to_bf16(da);
-          acc.v[mi][ni][r] = __uint_as_float((uint32_t)f32_to_bf16(db) | ((uint32_t)f32_to_bf16(h) << 16));
-        }
+    // dh rows, padding rows included (their do rows are zero)
+    stage<TL>(acc, lds, ld, 0);
     __syncthreads();
-    const int vr = min(TL::BM, rows_pad - m0);
-    char* DA = p.DADB + (int64_t)(row0 + m0) * p.dadb_row_bytes + (int64_t)n0 * 2;
-    copy_rows<TL>(lds, ld, cpr, vr, [&](int r) { return DA + (int64_t)r * p.dadb_row_bytes; });
-    __syncthreads();
-    stage<TL>(acc, lds, ld, 1);
-    __syncthreads();
-    char* DB = DA + (int64_t)p.F * 2;
-    copy_rows<TL>(lds, ld, cpr, vr, [&](int r) { return DB + (int64_t)r * p.dadb_row_bytes; });
-    __syncthreads();
-    stage<TL>(acc, lds, ld, 2);
-    __syncthreads();
-    char* H = p.H + (int64_t)(row0 + m0) * p.h_row_bytes + (int64_t)n0 * 2;
-    copy_rows<TL>(lds, ld, cpr, vr, [&](int r) { return H + (int64_t)r * p.h_row_bytes; });
+    char* C = p.C + (int64_t)(row0 + m0) * p.c_row_bytes + (int64_t)n0 * 2;
+    copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows_pad - m0), [&](int r) { return C + (int64_t)r * p.c_row_bytes; });
   } else {
     stage<TL>(acc, lds, ld, 0);
     __syncthreads();

@@ -99,7 +99,8 @@ __device__ __forceinline__ void read_frags_t(const char* sa, const char* sb, int
 // its stage, then tile kt's MFMAs with the second half's fragment reads
 // interleaved.  A row source advances by a_kstep / b_kstep bytes per K tile
 // (128 for a row-major operand; 64 k-rows for a K-major one).  Ends with a
-// barrier so the caller may reuse the LDS.
+// barrier so the caller may reuse the LDS.  (Spreading the loads among the
+// MFMAs, as the forward's core does, measured slower here.)
 template <class TL, bool AK, bool BK>
 __device__ __forceinline__ void mainloop_t(const RowSrc<TL::A_INS>& a_src, const RowSrc<TL::B_INS>& b_src,
                                            int ktiles, char* lds, Acc<TL>& acc, int64_t a_kstep,

@@ -157,6 +157,12 @@ struct RaggedGemm {
   int E, F, K, N;
   char* C;
   int64_t c_row_bytes;
+  // the backward's SwiGLU epilogue: dh rows in (bf16), h rows out; C gets
+  // [da | db]
+  const char* dH;
+  int64_t dh_row_bytes;
+  char* H;
+  int64_t h_row_bytes;
 };
 // M rows per tile and N columns (features for the SwiGLU) per tile.
 int ragged_tile_rows();
@@ -164,9 +170,10 @@ int ragged_gate_up_cols();
 int ragged_down_cols();
 hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
 hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
-// The forward SwiGLU's gate and up pre-activations (no activation), fp32:
-// row i of C gets a at columns [0, F) and b at [F, 2F) (backward recompute).
-hipError_t launch_ragged_preact_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
+// The backward's recompute of the SwiGLU pre-activations a = u W_g^T,
+// b = u W_u^T (fp32, never stored) with the SwiGLU backward in the
+// epilogue: from dh (g.dH) it writes da | db (g.C) and h (g.H), bf16.
+hipError_t launch_ragged_swiglu_bwd_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 // Routed-path backward (bf16).  Row moves and indices (backward.hip):
@@ -210,14 +217,8 @@ struct BwdDgrad {
   const char* W0;         // [E][K][N]: W_d (dh) or W_g (du)
   const char* W1;         // du: W_u
   int E, K, N, F;
-  // dh epilogue
-  const char* AB;         // fp32 pre-activations [a | b], ab_row_bytes apart
-  int64_t ab_row_bytes;
-  char* DADB;             // [da | db]
-  int64_t dadb_row_bytes;
-  char* H;
-  int64_t h_row_bytes;
-  // du epilogue: row i -> C + c_index[i] * c_row_bytes
+  // output: row i -> C + i * c_row_bytes (dh, padded rows included), or
+  // C + c_index[i] * c_row_bytes (du, kept rows only)
   char* C;
   int64_t c_row_bytes;
   const int32_t* c_index;

@@ -240,7 +240,7 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   bx.take(16);              // list lengths
   bx.take(R * L * 2);       // u rows
   bx.take(R * L * 2);       // do rows
-  bx.take(R * 2 * F * 4);   // pre-activations a | b (fp32)
+  bx.take(R * F * 2);       // dh
   bx.take(R * 2 * F * 2);   // da | db
   bx.take(R * F * 2);       // h
   p->experts_bwd_ws_bytes = bx.used;
@@ -901,7 +901,7 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* p
   int32_t* ntiles = static_cast<int32_t*>(cv.take(16));
   char* U = static_cast<char*>(cv.take(R * L * 2));
   char* DO = static_cast<char*>(cv.take(R * L * 2));
-  char* AB = static_cast<char*>(cv.take(R * 2 * F * 4));
+  char* DH = static_cast<char*>(cv.take(R * F * 2));
   char* DADB = static_cast<char*>(cv.take(R * 2 * F * 2));
   char* H = static_cast<char*>(cv.take(R * F * 2));
   const int bm = moe::bwd_dgrad_rows();
@@ -923,24 +923,7 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* p
                                 offsets + E, R, DO, s);
   if (e == hipSuccess && m) e = m->mark(s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  // recompute a = u W_g^T, b = u W_u^T
-  moe::RaggedGemm g{};
-  g.A = U;
-  g.a_row_bytes = L * 2;
-  g.offsets = offsets;
-  g.list = list_pre;
-  g.ntiles = ntiles;
-  g.W0 = static_cast<const char*>(wg);
-  g.W1 = static_cast<const char*>(wu);
-  g.E = E;
-  g.F = (int)F;
-  g.K = (int)L;
-  g.C = AB;
-  g.c_row_bytes = 2 * F * 4;
-  e = moe::launch_ragged_preact_bf16(g, epre, s);
-  if (e == hipSuccess && m) e = m->mark(s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  // dh = do W_d and the SwiGLU backward
+  // dh = do W_d
   moe::BwdDgrad d{};
   d.A = DO;
   d.a_row_bytes = L * 2;
@@ -953,13 +936,30 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* p
   d.K = (int)L;
   d.N = (int)F;
   d.F = (int)F;
-  d.AB = AB;
-  d.ab_row_bytes = 2 * F * 4;
-  d.DADB = DADB;
-  d.dadb_row_bytes = 2 * F * 2;
-  d.H = H;
-  d.h_row_bytes = F * 2;
+  d.C = DH;
+  d.c_row_bytes = F * 2;
   e = moe::launch_bwd_dh(d, edh, s);
+  if (e == hipSuccess && m) e = m->mark(s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // recompute a = u W_g^T, b = u W_u^T; SwiGLU backward: da, db, h
+  moe::RaggedGemm g{};
+  g.A = U;
+  g.a_row_bytes = L * 2;
+  g.offsets = offsets;
+  g.list = list_pre;
+  g.ntiles = ntiles;
+  g.W0 = static_cast<const char*>(wg);
+  g.W1 = static_cast<const char*>(wu);
+  g.E = E;
+  g.F = (int)F;
+  g.K = (int)L;
+  g.C = DADB;
+  g.c_row_bytes = 2 * F * 2;
+  g.dH = DH;
+  g.dh_row_bytes = F * 2;
+  g.H = H;
+  g.h_row_bytes = F * 2;
+  e = moe::launch_ragged_swiglu_bwd_bf16(g, epre, s);
   if (e == hipSuccess && m) e = m->mark(s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   // du = da W_g + db W_u, rows back to their pool slots
