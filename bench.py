@@ -8,8 +8,9 @@ dispatch with both caps, receiver binning, grouped SwiGLU experts, combine,
 up-projection and shared experts) over one batch of seeded synthetic inputs
 already resident in HBM.  Prints one JSON line.  --dropless times the
 dropless ragged variant; --backward times the routed path's backward
-(moe_backward_routed: gate, row and weight gradients for one forward call's
-routing, a seeded dL/dy_latent, forward state resident).
+(moe_backward_routed, or moe_backward_dropless with --dropless: gate, row and
+weight gradients for one forward call's routing, a seeded dL/dy_latent,
+forward state resident).
 
 Stage durations come from HIP events the library records between its kernel
 launches on the stream it launches them on (moe_forward_profiled), averaged
@@ -181,18 +182,23 @@ def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
                                       host["w_down"][e].to(torch.float64).numpy())
     if backward:
         # the saved state of the sample's own forward is not timed
-        r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
-                           send_cap=w.send_cap, recv_cap=w.recv_cap)
+        if dropless:
+            r = oracle.forward_dropless(x, wt, top_k=w.top_k)
+            keep = np.zeros(r["topk_idx"].shape, dtype=np.int64)
+        else:
+            r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
+                               send_cap=w.send_cap, recv_cap=w.recv_cap)
+            keep = r["assignment"]["recv_slot"]
         dy = f64(dy_latent[:n_tok])
         t0 = time.perf_counter()
-        g = oracle.routed_backward(r["z"], r["topk_idx"], r["gates"], r["assignment"]["recv_slot"],
+        g = oracle.routed_backward(r["z"], r["topk_idx"], r["gates"], keep,
                                    wt["expert_weights"], dy, w.n_experts, o=r["expert_out"],
                                    experts=())
         dt = time.perf_counter() - t0
         assert g["dz"].shape == (n_tok, w.d_latent)
         what = (f"routed-path backward (dz, d_logits and every present expert's weight "
                 f"gradients, computed and discarded) of the first {n_tok} tokens of the {w.name} "
-                f"inputs as their own batch (caps for {n_tok} tokens)")
+                f"inputs as their own batch ({'no caps' if dropless else f'caps for {n_tok} tokens'})")
     else:
         t0 = time.perf_counter()
         if dropless:
@@ -235,8 +241,6 @@ def main():
     ap.add_argument("--stage", default="expert_gate_up", help="stage for --summarize-pmc")
     ap.add_argument("--pmc-command", default="", help="command recorded by --summarize-pmc")
     args = ap.parse_args()
-    if args.dropless and args.backward:
-        raise SystemExit("--backward times the capped path's backward; drop --dropless")
     run_name = args.workload + ("_dropless" if args.dropless else "") + ("_backward" if args.backward else "")
     if args.cpu_tokens is None:
         args.cpu_tokens = 64 if args.backward else 256
@@ -269,18 +273,18 @@ def main():
     x = inp["x"]
     weights = {k: v for k, v in inp.items() if k != "x"}
     dy = None
-    if args.dropless:
-        fwd = rcd.ForwardDropless(cfg, weights, dev)
-        nst = rcd.dropless_stage_count()
-        stages = rcd.abi.DROPLESS_STAGES
-        step = fwd
-    elif args.backward:
-        fwd = rcd.Forward(cfg, weights, dev, taps=True)
+    if args.backward:
+        fwd = (rcd.ForwardDropless if args.dropless else rcd.Forward)(cfg, weights, dev, taps=True)
         fwd(x)           # the forward call whose gradient is taken: state saved
         dy = synth.grad_latent(w, args.seed, device=dev)
         step = rcd.BackwardRouted(fwd)
         nst = rcd.backward_stage_count()
         stages = rcd.abi.BACKWARD_STAGES
+    elif args.dropless:
+        fwd = rcd.ForwardDropless(cfg, weights, dev)
+        nst = rcd.dropless_stage_count()
+        stages = rcd.abi.DROPLESS_STAGES
+        step = fwd
     else:
         fwd = rcd.Forward(cfg, weights, dev)
         nst = rcd.stage_count()
@@ -325,7 +329,7 @@ def main():
             per[s] += ev[i][j].elapsed_time(ev[i][j + 1]) / K
     kept, sd, rd = [int(v) for v in fwd.counts.cpu().tolist()]
     sent = kept + rd
-    work = stage_work(w, kept, sent, dropless=args.dropless, backward=args.backward)
+    work = stage_work(w, kept, sent, dropless=args.dropless and not args.backward, backward=args.backward)
     peak_f = PEAK_TFLOPS[w.dtype]
     st_out = {}
     for s in stages:

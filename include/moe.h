@@ -113,6 +113,9 @@ typedef struct {
   int64_t backward_rows;              /* padded expert-major rows the backward works in */
   int64_t experts_bwd_ws_bytes;       /* workspace of moe_experts_backward              */
   int64_t backward_ws_bytes;          /* workspace of moe_backward_routed               */
+  int64_t dropless_backward_rows;     /* the same for the dropless variant (*_dropless) */
+  int64_t dropless_experts_bwd_ws_bytes; /* workspace of moe_experts_backward_dropless  */
+  int64_t dropless_backward_ws_bytes; /* workspace of moe_backward_dropless             */
 } moe_plan;
 
 /* Weights of one branch (device pointers, element type = dtype unless noted). */
@@ -430,6 +433,50 @@ moe_status moe_backward_routed_profiled(const moe_config* cfg, const moe_weights
                                         float* d_logits, void* dw_gate, void* dw_up,
                                         void* dw_down, void* ws, size_t ws_bytes, void* stream,
                                         void* const* stage_events, int32_t n_events);
+
+/* Backward of the dropless variant: the same transposes over its
+   expert-ordered rows (every assignment kept).  The experts' backward takes
+   xs and expert_offsets from moe_dispatch_dropless; the stages of
+   moe_backward_dropless are those of moe_backward_routed. */
+
+/* d_gates[t][j] = <dy_latent[t], expert_out[row_of[t][j]]> (0 where
+   row_of < 0); d_expert_out (out) [T*k][L]: gates[t][j] * dy_latent[t] at
+   row row_of[t][j]; rows without an assignment are not written. */
+moe_status moe_combine_backward_dropless(const moe_config* cfg, const void* expert_out,
+                                         const int32_t* row_of, const float* gates,
+                                         const void* dy_latent, float* d_gates,
+                                         void* d_expert_out, void* stream);
+
+/* d_xs (out) [T*k][L]: du of every row below expert_offsets[E]; dw_* (out)
+   as in moe_experts_backward.  ws at least dropless_experts_bwd_ws_bytes,
+   256-byte aligned. */
+moe_status moe_experts_backward_dropless(const moe_config* cfg, const void* xs,
+                                         const int32_t* expert_offsets, const void* w_gate,
+                                         const void* w_up, const void* w_down,
+                                         const void* d_expert_out, void* d_xs, void* dw_gate,
+                                         void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                         void* stream);
+
+/* dz (out) [T][L]: dz[t] = sum over j with row_of[t][j] >= 0 of
+   d_xs[row_of[t][j]], fp32 accumulation in j order. */
+moe_status moe_dispatch_backward_dropless(const moe_config* cfg, const int32_t* row_of,
+                                          const void* d_xs, void* dz, void* stream);
+
+/* The chain (combine, experts, dispatch, route backward): saved (host
+   struct) names the dropless forward's topk_idx, gates, row_of,
+   expert_offsets, xs and expert_out (all required).  ws at least
+   dropless_backward_ws_bytes, 256-byte aligned. */
+moe_status moe_backward_dropless(const moe_config* cfg, const moe_weights* w,
+                                 const moe_dropless_taps* saved, const void* dy_latent, void* dz,
+                                 float* d_logits, void* dw_gate, void* dw_up, void* dw_down,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* moe_backward_dropless recording stage_events as moe_forward_profiled does. */
+moe_status moe_backward_dropless_profiled(const moe_config* cfg, const moe_weights* w,
+                                          const moe_dropless_taps* saved, const void* dy_latent,
+                                          void* dz, float* d_logits, void* dw_gate, void* dw_up,
+                                          void* dw_down, void* ws, size_t ws_bytes, void* stream,
+                                          void* const* stage_events, int32_t n_events);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,7 @@ from . import abi
 __all__ = ["make_config", "plan", "route", "dispatch", "experts", "combine", "forward",
            "dispatch_dropless", "experts_dropless", "combine_dropless", "forward_dropless",
            "combine_backward", "experts_backward", "dispatch_backward", "route_backward",
+           "combine_backward_dropless", "experts_backward_dropless", "dispatch_backward_dropless",
            "BackwardRouted", "library", "MoeError"]
 
 MoeError = abi.MoeError
@@ -379,16 +380,18 @@ def route_backward(cfg, topk_idx, gates, d_gates, d_logits=None):
 
 
 class BackwardRouted:
-    """Reusable routed-path backward bound to a Forward built with taps=True:
-    its saved routing, pools and expert outputs feed the gradient."""
+    """Reusable routed-path backward bound to a Forward (or ForwardDropless)
+    built with taps=True: its saved routing, rows and expert outputs feed the
+    gradient (moe_backward_routed, or moe_backward_dropless)."""
 
-    def __init__(self, fwd: "Forward"):
+    def __init__(self, fwd):
         if fwd.taps is None:
             raise ValueError("the forward must keep its taps (taps=True)")
         cfg, dev = fwd.cfg, fwd.y.device
         self.cfg, self.fwd = cfg, fwd
         self.p = fwd.p
-        self.ws = _ws(self.p["backward_ws_bytes"], dev)
+        self.dropless = isinstance(fwd, ForwardDropless)
+        self.ws = _ws(self.p["dropless_backward_ws_bytes" if self.dropless else "backward_ws_bytes"], dev)
         self.dz = torch.empty((cfg.T, cfg.d_latent), dtype=_tdt(cfg), device=dev)
         self.d_logits = torch.empty((cfg.T, cfg.n_experts), dtype=torch.float32, device=dev)
         w = fwd.w
@@ -402,15 +405,58 @@ class BackwardRouted:
                 _stream(dy_latent.device))
 
     def __call__(self, dy_latent: torch.Tensor):
-        abi.check("moe_backward_routed", library().moe_backward_routed(*self._args(dy_latent)))
+        name = "moe_backward_dropless" if self.dropless else "moe_backward_routed"
+        abi.check(name, getattr(library(), name)(*self._args(dy_latent)))
         return self.dz, self.d_logits, self.dw
 
     def profiled(self, dy_latent: torch.Tensor, events):
         arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
-        abi.check("moe_backward_routed_profiled", library().moe_backward_routed_profiled(
-            *self._args(dy_latent), arr, len(events)))
+        name = "moe_backward_dropless_profiled" if self.dropless else "moe_backward_routed_profiled"
+        abi.check(name, getattr(library(), name)(*self._args(dy_latent), arr, len(events)))
         return self.dz, self.d_logits, self.dw
 
 
 def backward_stage_count() -> int:
     return library().moe_backward_routed_stage_count()
+
+
+def combine_backward_dropless(cfg, expert_out, row_of, gates, dy_latent, d_gates=None,
+                              d_expert_out=None):
+    """(d_gates [T, k] fp32, d_expert_out [T*k, L]) = transpose of combine_dropless."""
+    dev = dy_latent.device
+    if d_gates is None:
+        d_gates = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    if d_expert_out is None:
+        d_expert_out = torch.empty_like(expert_out)
+    abi.check("moe_combine_backward_dropless", library().moe_combine_backward_dropless(
+        C.byref(cfg), _ptr(expert_out), _ptr(row_of), _ptr(gates), _ptr(dy_latent), _ptr(d_gates),
+        _ptr(d_expert_out), _stream(dev)))
+    return d_gates, d_expert_out
+
+
+def experts_backward_dropless(cfg, xs, expert_offsets, w_gate, w_up, w_down, d_expert_out,
+                              d_xs=None, dw=None):
+    """(d_xs [T*k, L], (dw_gate, dw_up, dw_down)) = transpose of experts_dropless."""
+    p = plan(cfg)
+    dev = xs.device
+    if d_xs is None:
+        d_xs = torch.empty_like(xs)
+    if dw is None:
+        dw = (torch.empty_like(w_gate), torch.empty_like(w_up), torch.empty_like(w_down))
+    ws = _ws(p["dropless_experts_bwd_ws_bytes"], dev)
+    abi.check("moe_experts_backward_dropless", library().moe_experts_backward_dropless(
+        C.byref(cfg), _ptr(xs), _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(d_expert_out), _ptr(d_xs), _ptr(dw[0]), _ptr(dw[1]), _ptr(dw[2]), _ptr(ws),
+        ws.numel(), _stream(dev)))
+    return d_xs, dw
+
+
+def dispatch_backward_dropless(cfg, row_of, d_xs, dz=None):
+    """dz [T, L] = transpose of dispatch_dropless."""
+    dev = d_xs.device
+    if dz is None:
+        dz = torch.empty((cfg.T, cfg.d_latent), dtype=_tdt(cfg), device=dev)
+    abi.check("moe_dispatch_backward_dropless", library().moe_dispatch_backward_dropless(
+        C.byref(cfg), _ptr(row_of), _ptr(d_xs), _ptr(dz), _stream(dev)))
+    return dz
+

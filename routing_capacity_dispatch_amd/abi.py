@@ -37,7 +37,8 @@ class MoePlan(C.Structure):
         "max_expert_rows", "dispatch_ws_bytes", "experts_ws_bytes", "forward_ws_bytes",
         "dropless_rows", "dropless_dispatch_ws_bytes", "dropless_experts_ws_bytes",
         "dropless_forward_ws_bytes", "backward_rows", "experts_bwd_ws_bytes",
-        "backward_ws_bytes")]
+        "backward_ws_bytes", "dropless_backward_rows", "dropless_experts_bwd_ws_bytes",
+        "dropless_backward_ws_bytes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -100,6 +101,17 @@ SIGNATURES = {
                                       C.POINTER(MoeTaps), _P, _P, _P, _P, _P, _P, _P,
                                       C.c_size_t, _P]),
     "moe_backward_routed_stage_count": (C.c_int32, []),
+    "moe_combine_backward_dropless": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_experts_backward_dropless": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P,
+                                                _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_dispatch_backward_dropless": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P]),
+    "moe_backward_dropless": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights),
+                                        C.POINTER(MoeDroplessTaps), _P, _P, _P, _P, _P, _P, _P,
+                                        C.c_size_t, _P]),
+    "moe_backward_dropless_profiled": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights),
+                                                 C.POINTER(MoeDroplessTaps), _P, _P, _P, _P, _P,
+                                                 _P, _P, C.c_size_t, _P, C.POINTER(C.c_void_p),
+                                                 C.c_int32]),
     "moe_backward_routed_profiled": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoeWeights),
                                                C.POINTER(MoeTaps), _P, _P, _P, _P, _P, _P, _P,
                                                C.c_size_t, _P, C.POINTER(C.c_void_p),

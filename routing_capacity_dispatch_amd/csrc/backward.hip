@@ -50,6 +50,39 @@ __global__ __launch_bounds__(64) void bwd_gidx_kernel(const int32_t* __restrict_
   for (int r = off + lane; r < offsets[e + 1]; r += 64) gidx[r] = -1;
 }
 
+// The dropless variant's layout: expert e's rows are [off[e], off[e+1]) of
+// the expert-ordered buffer; counts and the padded offsets as above.
+__global__ __launch_bounds__(1024) void bwd_offsets_ragged_kernel(const int32_t* __restrict__ off, int E, int64_t n,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets) {
+  __shared__ int part[16];
+  __shared__ int total;
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+    const int64_t a = min(max((int64_t)off[e], (int64_t)0), n), b = min(max((int64_t)off[e + 1], a), n);
+    c = (int)(b - a);
+  }
+  const int ex = block_excl_scan_1024((c + 63) & ~63, part, &total);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = ex;
+  }
+  if (e == 0) offsets[E] = total;
+}
+
+// Padded row i of expert e -> row off[e] + r of the expert-ordered buffer, or
+// -1 for padding.
+__global__ __launch_bounds__(64) void bwd_gidx_ragged_kernel(const int32_t* __restrict__ off,
+                                                             const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ gidx) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int c = counts[e], first = off[e], o = offsets[e];
+  for (int r = lane; r < c; r += 64) gidx[o + r] = first + r;
+  for (int r = o + c + lane; r < offsets[e + 1]; r += 64) gidx[r] = -1;
+}
+
 // dst row i = the pool row gidx[i] (block = i / block_rows at block_bytes
 // apart, rows row_bytes apart inside a block), or zeros where gidx[i] < 0.
 // 16-byte chunks, grid-stride.
@@ -73,7 +106,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 }
 
 // Transpose of combine, one wavefront per token t: for each receiver-kept
-// assignment j, d_gates[t, j] = <dy[t], o[t, j]> (fp32, lane partial sums
+// assignment j (dropless: each assignment with a row, row_of >= 0), d_gates[t, j] = <dy[t], o[t, j]> (fp32, lane partial sums
 // in chunk order, then a butterfly over the wavefront) and the row
 // g[t, j] * dy[t] goes to the pool slot the forward read o[t, j] from.  A
 // dropped assignment gets d_gates = 0 and no row.
@@ -94,13 +127,17 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   }
   for (int j = 0; j < k; ++j) {
     const int64_t q = t * k + j;
-    const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
-    const bool kept = rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send;
-    if (!kept) {
+    int64_t row = -1;
+    if (a.row_of) {  // dropless: the assignment's row in expert order
+      row = a.row_of[q];
+    } else {
+      const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
+      if (rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send) row = (w * a.P + e / epp) * a.cap_send + ps;
+    }
+    if (row < 0) {
       if (lane == 0) a.d_gates[q] = 0.0f;
       continue;
     }
-    const int64_t row = (w * a.P + e / epp) * a.cap_send + ps;
     const float g = a.gates[q];
     const char* o = static_cast<const char*>(a.expert_out) + row * a.row_bytes;
     char* d = static_cast<char*>(a.d_expert_out) + row * a.row_bytes;
@@ -168,6 +205,15 @@ hipError_t launch_bwd_layout(const int32_t* bank_rows, const int32_t* expert_cou
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   bwd_gidx_kernel<<<E, 64, 0, s>>>(bank_rows, expert_count, offsets, E, P, W, (int)cap_send, (int)cap_recv, gidx);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_layout_ragged(const int32_t* expert_offsets, int E, int64_t n, int32_t* counts,
+                                    int32_t* offsets, int32_t* gidx, hipStream_t s) {
+  bwd_offsets_ragged_kernel<<<1, 1024, 0, s>>>(expert_offsets, E, n, counts, offsets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_gidx_ragged_kernel<<<E, 64, 0, s>>>(expert_offsets, counts, offsets, gidx);
   return hipGetLastError();
 }
 

@@ -183,14 +183,19 @@ hipError_t launch_ragged_swiglu_bwd_bf16(const RaggedGemm& g, int64_t max_entrie
 hipError_t launch_bwd_layout(const int32_t* bank_rows, const int32_t* expert_count, int E, int P, int W,
                              int64_t cap_send, int64_t cap_recv, int32_t* counts, int32_t* offsets, int32_t* gidx,
                              hipStream_t s);
+// The same from the dropless variant's expert offsets over n rows:
+// gidx[i] = the row of the expert-ordered buffer, -1 for padding.
+hipError_t launch_bwd_layout_ragged(const int32_t* expert_offsets, int E, int64_t n, int32_t* counts,
+                                    int32_t* offsets, int32_t* gidx, hipStream_t s);
 // dst row i = pool row gidx[i] of src (blocks of block_rows rows) or zeros;
 // *nrows rows (device), at most max_rows.
 hipError_t launch_gather_rows(const void* src, int block_rows, int64_t block_bytes, int64_t row_bytes,
                               const int32_t* gidx, const int32_t* nrows, int64_t max_rows, void* dst,
                               hipStream_t s);
 struct CombineBwdArgs {
-  const void* expert_out;  // [W][P][C_send][L]
+  const void* expert_out;  // [W][P][C_send][L], or [T*k][L] with row_of
   const void* dy;          // [T][L]
+  const int32_t* row_of;   // dropless: row of each assignment (NULL: pool slots)
   const int32_t* topk;
   const int32_t* pool_slot;
   const int32_t* recv_slot;

@@ -244,6 +244,32 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   bx.take(R * 2 * F * 2);   // da | db
   bx.take(R * F * 2);       // h
   p->experts_bwd_ws_bytes = bx.used;
+  // ... and for the dropless variant, over its T*k rows
+  const int64_t Rd = n + 63 * E;
+  int64_t dpre, ddh, ddu;
+  backward_entries(c, Rd, &dpre, &ddh, &ddu);
+  if (Rd > kI32Max || dpre > kI32Max / 3 || ddh > kI32Max / 3 || ddu > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+  p->dropless_backward_rows = Rd;
+  Carver dbx{nullptr, 0};
+  dbx.take(E * 4);
+  dbx.take((E + 1) * 4);
+  dbx.take(Rd * 4);
+  dbx.take(dpre * 12);
+  dbx.take(ddh * 12);
+  dbx.take(ddu * 12);
+  dbx.take(16);
+  dbx.take(Rd * L * 2);
+  dbx.take(Rd * L * 2);
+  dbx.take(Rd * F * 2);
+  dbx.take(Rd * 2 * F * 2);
+  dbx.take(Rd * F * 2);
+  p->dropless_experts_bwd_ws_bytes = dbx.used;
+  Carver dbb{nullptr, 0};
+  dbb.take(T * k * 4);       // d_gates
+  dbb.take(n * L * eb);      // d_expert_out
+  dbb.take(n * L * eb);      // d_xs
+  dbb.take(p->dropless_experts_bwd_ws_bytes);
+  p->dropless_backward_ws_bytes = dbb.used;
   Carver bb{nullptr, 0};
   bb.take(T * k * 4);              // d_gates
   bb.take(p->expert_out_bytes);    // d_expert_out
@@ -883,12 +909,22 @@ moe_status run_combine_bwd(const moe_config* c, const moe_plan& p, const void* e
   return hip_status(moe::launch_combine_bwd(a, s));
 }
 
-moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* pools, const int32_t* bank_rows,
-                           const int32_t* expert_count, const void* wg, const void* wu, const void* wd,
-                           const void* d_expert_out, void* d_pool_rows, void* dwg, void* dwu, void* dwd,
-                           void* ws, hipStream_t s, Marks* m) {
+// Where the experts' backward finds its rows: the capped path's pools and
+// bank lists, or the dropless variant's expert-ordered buffers.
+struct BwdRows {
+  const int32_t* bank_rows;       // capped
+  const int32_t* expert_count;
+  const int32_t* expert_offsets;  // dropless (non-NULL selects it)
+  const void* u;                  // pools, or xs
+  const void* d_out;              // d_expert_out
+  void* d_in;                     // du out: d_pool_rows, or d_xs
+};
+
+moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const BwdRows& src, const void* wg, const void* wu,
+                           const void* wd, void* dwg, void* dwu, void* dwd, void* ws, hipStream_t s, Marks* m) {
   const int E = c->n_experts;
-  const int64_t L = c->d_latent, F = c->d_ff, R = p.backward_rows;
+  const bool ragged = src.expert_offsets != nullptr;
+  const int64_t L = c->d_latent, F = c->d_ff, R = ragged ? p.dropless_backward_rows : p.backward_rows;
   int64_t epre, edh, edu;
   backward_entries(c, R, &epre, &edh, &edu);
   Carver cv{static_cast<char*>(ws), 0};
@@ -905,8 +941,10 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* p
   char* DADB = static_cast<char*>(cv.take(R * 2 * F * 2));
   char* H = static_cast<char*>(cv.take(R * F * 2));
   const int bm = moe::bwd_dgrad_rows();
-  hipError_t e = moe::launch_bwd_layout(bank_rows, expert_count, E, c->n_pools, c->n_waves, p.cap_send,
-                                        p.cap_recv, counts, offsets, gidx, s);
+  hipError_t e = ragged ? moe::launch_bwd_layout_ragged(src.expert_offsets, E, p.dropless_rows, counts, offsets,
+                                                         gidx, s)
+                        : moe::launch_bwd_layout(src.bank_rows, src.expert_count, E, c->n_pools, c->n_waves,
+                                                 p.cap_send, p.cap_recv, counts, offsets, gidx, s);
   if (e == hipSuccess)
     e = moe::launch_ragged_tiles(offsets, E, bm, (int)ceil_div(F, moe::ragged_gate_up_cols()),
                                  (int)ceil_div(F, moe::bwd_dgrad_cols()), list_pre, list_dh, ntiles, s);
@@ -915,12 +953,15 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* p
                                  ntiles + 2, s);
   if (e == hipSuccess && m) e = m->mark(s);
   // u and do rows in the padded expert-major order (zero padding rows)
+  const int one_block = 0x7fffffff;  // the dropless buffers are one block of rows
   if (e == hipSuccess)
-    e = moe::launch_gather_rows(pools, (int)p.cap_send, p.pool_block_bytes, p.row_bytes, gidx, offsets + E, R, U,
-                                s);
+    e = ragged ? moe::launch_gather_rows(src.u, one_block, 0, p.row_bytes, gidx, offsets + E, R, U, s)
+               : moe::launch_gather_rows(src.u, (int)p.cap_send, p.pool_block_bytes, p.row_bytes, gidx, offsets + E,
+                                         R, U, s);
   if (e == hipSuccess)
-    e = moe::launch_gather_rows(d_expert_out, (int)p.cap_send, p.cap_send * p.row_bytes, p.row_bytes, gidx,
-                                offsets + E, R, DO, s);
+    e = ragged ? moe::launch_gather_rows(src.d_out, one_block, 0, p.row_bytes, gidx, offsets + E, R, DO, s)
+               : moe::launch_gather_rows(src.d_out, (int)p.cap_send, p.cap_send * p.row_bytes, p.row_bytes, gidx,
+                                         offsets + E, R, DO, s);
   if (e == hipSuccess && m) e = m->mark(s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   // dh = do W_d
@@ -977,7 +1018,7 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const void* p
   u.K = (int)F;
   u.N = (int)L;
   u.F = (int)F;
-  u.C = static_cast<char*>(d_pool_rows);
+  u.C = static_cast<char*>(src.d_in);
   u.c_row_bytes = p.row_bytes;
   u.c_index = gidx;
   e = moe::launch_bwd_du(u, edu, s);
@@ -1041,9 +1082,10 @@ moe_status backward_impl(const moe_config* cfg, const moe_weights* w, const moe_
   st = run_combine_bwd(cfg, p, sv->expert_out, sv->topk_idx, sv->pool_slot, sv->recv_slot, sv->gates, dy, d_gates,
                        d_expert_out, s);
   if (st == MOE_OK && m) st = hip_status(m->mark(s));
-  if (st == MOE_OK)
-    st = run_experts_bwd(cfg, p, sv->pools, sv->bank_rows, sv->expert_count, w->w_gate, w->w_up, w->w_down,
-                         d_expert_out, d_pool_rows, dwg, dwu, dwd, ews, s, m);
+  if (st == MOE_OK) {
+    const BwdRows src{sv->bank_rows, sv->expert_count, nullptr, sv->pools, d_expert_out, d_pool_rows};
+    st = run_experts_bwd(cfg, p, src, w->w_gate, w->w_up, w->w_down, dwg, dwu, dwd, ews, s, m);
+  }
   if (st == MOE_OK)
     st = run_dispatch_bwd(cfg, p, sv->topk_idx, sv->pool_slot, sv->recv_slot, d_pool_rows, dz, s);
   if (st == MOE_OK && m) st = hip_status(m->mark(s));
@@ -1080,8 +1122,9 @@ MOE_API moe_status moe_experts_backward(const moe_config* cfg, const void* pools
       !dw_gate || !dw_up || !dw_down)
     return MOE_ERR_INVALID_ARG;
   if (!ws || (int64_t)ws_bytes < p.experts_bwd_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
-  return run_experts_bwd(cfg, p, pools, bank_rows, expert_count, w_gate, w_up, w_down, d_expert_out, d_pool_rows,
-                         dw_gate, dw_up, dw_down, ws, static_cast<hipStream_t>(stream), nullptr);
+  const BwdRows src{bank_rows, expert_count, nullptr, pools, d_expert_out, d_pool_rows};
+  return run_experts_bwd(cfg, p, src, w_gate, w_up, w_down, dw_gate, dw_up, dw_down, ws,
+                         static_cast<hipStream_t>(stream), nullptr);
 }
 
 MOE_API moe_status moe_dispatch_backward(const moe_config* cfg, const int32_t* topk_idx, const int32_t* pool_slot,
@@ -1122,4 +1165,123 @@ MOE_API moe_status moe_backward_routed_profiled(const moe_config* cfg, const moe
     if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
   return backward_impl(cfg, w, saved, dy_latent, dz, d_logits, dw_gate, dw_up, dw_down, ws, ws_bytes, stream,
                        stage_events, n_events);
+}
+
+// ------------------------------------------------------------------ dropless backward
+namespace {
+
+moe_status run_combine_bwd_dropless(const moe_config* c, const moe_plan& p, const void* expert_out,
+                                    const int32_t* row_of, const float* gates, const void* dy, float* d_gates,
+                                    void* d_expert_out, hipStream_t s) {
+  moe::CombineBwdArgs a{};
+  a.expert_out = expert_out;
+  a.dy = dy;
+  a.row_of = row_of;
+  a.gates = gates;
+  a.T = c->T;
+  a.Tw = p.tokens_per_wave > 0 ? p.tokens_per_wave : 1;
+  a.k = c->top_k;
+  a.E = c->n_experts;
+  a.P = c->n_pools;
+  a.cap_send = p.cap_send;
+  a.row_bytes = p.row_bytes;
+  a.d_gates = d_gates;
+  a.d_expert_out = d_expert_out;
+  return hip_status(moe::launch_combine_bwd(a, s));
+}
+
+moe_status backward_dropless_impl(const moe_config* cfg, const moe_weights* w, const moe_dropless_taps* sv,
+                                  const void* dy, void* dz, float* d_logits, void* dwg, void* dwu, void* dwd,
+                                  void* ws, size_t ws_bytes, void* stream, void* const* events, int n_events) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!w || !sv || !w->w_gate || !w->w_up || !w->w_down || !dwg || !dwu || !dwd || !sv->expert_offsets)
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!sv->topk_idx || !sv->gates || !sv->row_of || !sv->xs || !sv->expert_out || !dy || !dz ||
+                     !d_logits))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.dropless_backward_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Marks marks{events, n_events, 0};
+  Marks* m = events ? &marks : nullptr;
+  Carver cv{static_cast<char*>(ws), 0};
+  const int64_t T = cfg->T, k = cfg->top_k, n = p.dropless_rows;
+  float* d_gates = static_cast<float*>(cv.take(T * k * 4));
+  void* d_expert_out = cv.take(n * p.row_bytes);
+  void* d_xs = cv.take(n * p.row_bytes);
+  void* ews = cv.take(p.dropless_experts_bwd_ws_bytes);
+  hipError_t e = m ? m->mark(s) : hipSuccess;
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  st = run_combine_bwd_dropless(cfg, p, sv->expert_out, sv->row_of, sv->gates, dy, d_gates, d_expert_out, s);
+  if (st == MOE_OK && m) st = hip_status(m->mark(s));
+  if (st == MOE_OK) {
+    const BwdRows src{nullptr, nullptr, sv->expert_offsets, sv->xs, d_expert_out, d_xs};
+    st = run_experts_bwd(cfg, p, src, w->w_gate, w->w_up, w->w_down, dwg, dwu, dwd, ews, s, m);
+  }
+  if (st == MOE_OK)
+    st = hip_status(moe::launch_ragged_combine(cfg->dtype, d_xs, sv->row_of, nullptr, T, (int)k, p.row_bytes, dz, s));
+  if (st == MOE_OK && m) st = hip_status(m->mark(s));
+  if (st == MOE_OK)
+    st = hip_status(moe::launch_route_bwd(sv->topk_idx, sv->gates, d_gates, T, (int)k, cfg->n_experts, d_logits, s));
+  if (st == MOE_OK && m) st = hip_status(m->mark(s));
+  return st;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_combine_backward_dropless(const moe_config* cfg, const void* expert_out,
+                                                 const int32_t* row_of, const float* gates, const void* dy_latent,
+                                                 float* d_gates, void* d_expert_out, void* stream) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!expert_out || !row_of || !gates || !dy_latent || !d_gates || !d_expert_out))
+    return MOE_ERR_INVALID_ARG;
+  return run_combine_bwd_dropless(cfg, p, expert_out, row_of, gates, dy_latent, d_gates, d_expert_out,
+                                  static_cast<hipStream_t>(stream));
+}
+
+MOE_API moe_status moe_experts_backward_dropless(const moe_config* cfg, const void* xs, const int32_t* expert_offsets,
+                                                 const void* w_gate, const void* w_up, const void* w_down,
+                                                 const void* d_expert_out, void* d_xs, void* dw_gate, void* dw_up,
+                                                 void* dw_down, void* ws, size_t ws_bytes, void* stream) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!xs || !d_expert_out || !d_xs)) return MOE_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.dropless_experts_bwd_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+  const BwdRows src{nullptr, nullptr, expert_offsets, xs, d_expert_out, d_xs};
+  return run_experts_bwd(cfg, p, src, w_gate, w_up, w_down, dw_gate, dw_up, dw_down, ws,
+                         static_cast<hipStream_t>(stream), nullptr);
+}
+
+MOE_API moe_status moe_dispatch_backward_dropless(const moe_config* cfg, const int32_t* row_of, const void* d_xs,
+                                                  void* dz, void* stream) {
+  moe_plan p;
+  moe_status st = check_backward(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!row_of || !d_xs || !dz)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_ragged_combine(cfg->dtype, d_xs, row_of, nullptr, cfg->T, cfg->top_k, p.row_bytes,
+                                               dz, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_backward_dropless(const moe_config* cfg, const moe_weights* w, const moe_dropless_taps* saved,
+                                         const void* dy_latent, void* dz, float* d_logits, void* dw_gate,
+                                         void* dw_up, void* dw_down, void* ws, size_t ws_bytes, void* stream) {
+  return backward_dropless_impl(cfg, w, saved, dy_latent, dz, d_logits, dw_gate, dw_up, dw_down, ws, ws_bytes,
+                                stream, nullptr, 0);
+}
+
+MOE_API moe_status moe_backward_dropless_profiled(const moe_config* cfg, const moe_weights* w,
+                                                  const moe_dropless_taps* saved, const void* dy_latent, void* dz,
+                                                  float* d_logits, void* dw_gate, void* dw_up, void* dw_down,
+                                                  void* ws, size_t ws_bytes, void* stream,
+                                                  void* const* stage_events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && !stage_events)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+  return backward_dropless_impl(cfg, w, saved, dy_latent, dz, d_logits, dw_gate, dw_up, dw_down, ws, ws_bytes,
+                                stream, stage_events, n_events);
 }

@@ -210,7 +210,8 @@ __global__ __launch_bounds__(1024) void ragged_tiles_kernel(const int32_t* __res
 }
 
 // y_lat[t] = sum over j with a row of gates[t][j] * out[row_of[t][j]], fp32
-// accumulation in j order, one wavefront per token.
+// accumulation in j order, one wavefront per token.  gates == NULL: weight 1
+// (the transpose of the dropless dispatch).
 template <typename T>
 __global__ __launch_bounds__(256) void ragged_combine_kernel(const char* __restrict__ out,
                                                               const int32_t* __restrict__ row_of,
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256) void ragged_combine_kernel(const char* __restr
   float g = 0.0f;
   if (lane < k) {
     row = row_of[t * k + lane];
-    if (row >= 0) g = gates[t * k + lane];
+    if (row >= 0) g = gates ? gates[t * k + lane] : 1.0f;
   }
   combine_rows<T>(out, row, g, k, row_bytes, y + t * row_bytes);
 }

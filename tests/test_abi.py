@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header():
     # sizes implied by the header's field lists (natural alignment, no packing)
     assert C.sizeof(abi.MoeConfig) == 8 + 13 * 4 + 4 + 2 * 8 + 2 * 4
-    assert C.sizeof(abi.MoePlan) == 21 * 8
+    assert C.sizeof(abi.MoePlan) == 24 * 8
     assert C.sizeof(abi.MoeWeights) == 10 * 8
     assert C.sizeof(abi.MoeTaps) == 12 * 8
 
@@ -253,4 +253,29 @@ def test_backward_plan_and_validation(lib):
     assert lib.moe_backward_routed(C.byref(bf), C.byref(ww), nul, *([fake] * 6), fake,
                                    pb["backward_ws_bytes"], nul) == abi.MOE_ERR_INVALID_ARG
     assert lib.moe_backward_routed_stage_count() == len(abi.BACKWARD_STAGES)
+
+
+def test_dropless_backward_plan_and_validation(lib):
+    w = synth.workload("marin_16k")
+    p = rcd.plan(rcd.config_of(w))
+    n = w.T * w.top_k
+    assert p["dropless_backward_rows"] == n + 63 * w.n_experts
+    assert p["dropless_backward_ws_bytes"] >= p["dropless_experts_bwd_ws_bytes"] + 2 * n * w.d_latent * 2
+    nul = None
+    fake = C.c_void_p(0x100000)
+    bf = rcd.config_of(synth.workload("mid_bf16"))
+    pb = rcd.plan(bf)
+    assert lib.moe_combine_backward_dropless(C.byref(bf), fake, nul, *([fake] * 4), nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_backward_dropless(C.byref(bf), fake, fake, nul, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_experts_backward_dropless(C.byref(bf), *([fake] * 10), fake,
+                                             pb["dropless_experts_bwd_ws_bytes"] - 256, nul) == abi.MOE_ERR_WORKSPACE
+    f32 = rcd.config_of(synth.workload("tiny_fp32"))
+    assert lib.moe_dispatch_backward_dropless(C.byref(f32), fake, fake, fake, nul) == abi.MOE_ERR_UNSUPPORTED
+    ww = abi.MoeWeights(*([0x100000] * 10))
+    taps = abi.MoeDroplessTaps(*([0x100000] * 9))
+    assert lib.moe_backward_dropless(C.byref(bf), C.byref(ww), C.byref(taps), *([fake] * 6), fake,
+                                     pb["dropless_backward_ws_bytes"] - 1, nul) == abi.MOE_ERR_WORKSPACE
+    taps.row_of = None
+    assert lib.moe_backward_dropless(C.byref(bf), C.byref(ww), C.byref(taps), *([fake] * 6), fake,
+                                     pb["dropless_backward_ws_bytes"], nul) == abi.MOE_ERR_INVALID_ARG
 

@@ -210,3 +210,102 @@ def test_backward_full_size_sampled(name):
         _, gg, gu, gd = oracle.swiglu_backward(zr, f64(wg[e]), f64(wu[e]), f64(wd[e]), d_o)
         for got, want in zip(bwd.dw, (gg, gu, gd)):
             assert rowwise_rel_err(f64(got[e]), want) <= t_, e
+
+
+# ------------------------------------------------------------------ dropless
+def _run_dropless(w, seed, d):
+    cfg = rcd.config_of(w)
+    inp = synth.make_inputs(w, seed, device=d)
+    weights = {k: v for k, v in inp.items() if k != "x"}
+    fwd = rcd.ForwardDropless(cfg, weights, d, taps=True)
+    fwd(inp["x"])
+    dy = synth.grad_latent(w, seed, device=d)
+    bwd = rcd.BackwardRouted(fwd)
+    dz, d_logits, dw = bwd(dy)
+    torch.cuda.synchronize()
+    return cfg, inp, fwd, bwd, dy, dz, d_logits, dw
+
+
+def _saved_o_dropless(fwd, toks=None):
+    taps = fwd.tap_t
+    row_of = np_i(taps["row_of"])
+    toks = np.arange(row_of.shape[0]) if toks is None else np.asarray(toks)
+    r = row_of[toks]
+    o = f64(taps["expert_out"][torch.from_numpy(np.maximum(r, 0).reshape(-1)).to(taps["expert_out"].device)])
+    o = o.reshape(len(toks), r.shape[1], -1)
+    return np.where((r >= 0)[:, :, None], o, 0.0)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_dropless_mid(seed):
+    d = dev()
+    w = synth.workload("mid_bf16")
+    say("backward dropless mid_bf16", seed)
+    cfg, inp, fwd, bwd, dy, dz, d_logits, dw = _run_dropless(w, seed, d)
+    wt = oracle_weights(inp)
+    taps = fwd.tap_t
+    topk = np_i(taps["topk_idx"])
+    keep = np.zeros(topk.shape, dtype=np.int64)   # every assignment kept
+    ref = oracle.routed_backward(f64(taps["z"]), topk, np_f32(taps["gates"]).astype(np.float64), keep,
+                                 lambda e: (wt["w_gate"][e], wt["w_up"][e], wt["w_down"][e]), f64(dy),
+                                 w.n_experts, o=_saved_o_dropless(fwd), experts=range(w.n_experts))
+    t = tol(w.dtype)
+    assert rowwise_rel_err(f64(dz), ref["dz"]) <= t
+    assert rowwise_rel_err(np_f32(d_logits).astype(np.float64), ref["d_logits"]) <= t
+    for i in range(3):
+        got = f64(dw[i])
+        want = np.stack([ref["dw"][e][i] for e in range(w.n_experts)])
+        assert rowwise_rel_err(got.reshape(-1, got.shape[-1]), want.reshape(-1, want.shape[-1])) <= t, i
+
+
+def test_backward_dropless_components_compose_bitwise():
+    d = dev()
+    w = synth.workload("mid_bf16", T=1500)
+    say("backward dropless components")
+    cfg, inp, fwd, bwd, dy, dz, d_logits, dw = _run_dropless(w, 4, d)
+    t = fwd.tap_t
+    dg, deo = rcd.combine_backward_dropless(cfg, t["expert_out"], t["row_of"], t["gates"], dy)
+    dxs, dwc = rcd.experts_backward_dropless(cfg, t["xs"], t["expert_offsets"], fwd.w["w_gate"],
+                                             fwd.w["w_up"], fwd.w["w_down"], deo)
+    dzc = rcd.dispatch_backward_dropless(cfg, t["row_of"], dxs)
+    dlc = rcd.route_backward(cfg, t["topk_idx"], t["gates"], dg)
+    torch.cuda.synchronize()
+    assert torch.equal(dzc.view(torch.int16), dz.view(torch.int16))
+    assert torch.equal(dlc, d_logits)
+    for a, b in zip(dwc, dw):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_backward_dropless_full_size_sampled():
+    d = dev()
+    w = synth.workload("marin_16k")
+    say("backward dropless full size")
+    cfg, inp, fwd, bwd, dy, dz, d_logits, dw = _run_dropless(w, 0, d)
+    taps = fwd.tap_t
+    topk = np_i(taps["topk_idx"])
+    gates = np_f32(taps["gates"]).astype(np.float64)
+    toks = np.sort(np.random.default_rng(8).choice(w.T, 16, replace=False))
+    z = f64(taps["z"][torch.from_numpy(toks).to(d)])
+    dyt = f64(dy[torch.from_numpy(toks).to(d)])
+    o_saved = _saved_o_dropless(fwd, toks)
+    wg, wu, wd = (fwd.w[n] for n in ("w_gate", "w_up", "w_down"))
+    want_dz = np.zeros_like(z)
+    want_dg = np.zeros((len(toks), w.top_k))
+    for i, t in enumerate(toks):
+        for j in range(w.top_k):
+            e = int(topk[t, j])
+            W3 = [f64(m[e]) for m in (wg, wu, wd)]
+            want_dg[i, j] = dyt[i] @ o_saved[i, j]
+            du, _, _, _ = oracle.swiglu_backward(z[i:i + 1], *W3, gates[t, j] * dyt[i:i + 1])
+            want_dz[i] += du[0]
+    t_ = tol(w.dtype)
+    assert rowwise_rel_err(f64(dz[torch.from_numpy(toks).to(d)]), want_dz) <= t_
+    want_dl = oracle.scatter_logit_grad(topk[toks], oracle.gates_backward(gates[toks], want_dg), w.n_experts)
+    assert rowwise_rel_err(np_f32(d_logits[torch.from_numpy(toks).to(d)]).astype(np.float64), want_dl) <= t_
+    e = 11
+    rows, js = np.nonzero(topk == e)
+    zr = f64(taps["z"][torch.from_numpy(rows).to(d)])
+    d_o = gates[rows, js][:, None] * f64(dy[torch.from_numpy(rows).to(d)])
+    _, gg, gu, gd = oracle.swiglu_backward(zr, f64(wg[e]), f64(wu[e]), f64(wd[e]), d_o)
+    for got, want in zip(dw, (gg, gu, gd)):
+        assert rowwise_rel_err(f64(got[e]), want) <= t_
