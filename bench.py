@@ -53,7 +53,7 @@ COPY_KERNEL = ("copyBuffer",)
 # sources of the GEMM kernels: a measured traffic figure is used only while
 # they are unchanged
 KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "dispatch.hip",
-                  "gemm_kmajor.h", "gemm_bwd.hip", "backward.hip"]
+                  "gemm_bwd.hip", "backward.hip"]
 
 
 def kernel_source_hash():

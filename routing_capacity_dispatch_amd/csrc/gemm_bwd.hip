@@ -13,12 +13,14 @@
 //               read K-major: dW_d = do^T h, dW_g = da^T u, dW_u = db^T u,
 //               written in the weights' [out][in] layout
 //
-// dgrad tiles are 192 rows x 256 columns (8 wavefronts, 96 x 64 each) over
-// device-built tile lists like the forward's; wgrad tiles are 256 x 256 (8
-// wavefronts, 64 x 128 each), an expert's tiles dealt to one XCD.
+// dgrad tiles are 192 rows x 256 columns (8 wavefronts, 96 x 64 each, a
+// third LDS stage for the streaming weights) over device-built tile lists
+// like the forward's; wgrad tiles are 256 x 256 (8 wavefronts, 64 x 128
+// each), an expert's tiles dealt to one XCD.  dgrad runs the forward core's
+// split-barrier schedule with a K-major B operand; wgrad, with two K-major
+// operands, the plain two-stage one (gemm_core.h).
 #include "common.h"
 #include "gemm_core.h"
-#include "gemm_kmajor.h"
 #include "kernels.h"
 
 namespace moe {
@@ -31,11 +33,11 @@ using core::kload_col;
 using core::kload_row;
 using core::load_col;
 using core::load_row;
-using core::mainloop_t;
+using core::mainloop;
 using core::RowSrc;
 using core::uniform_ptr;
 
-using DgradTile = core::Tile<192, 256, 2, 4, 64, 2, 2>;
+using DgradTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;  // the weights stream: a third B stage
 using WgradTile = core::Tile<256, 256, 4, 2, 64, 2, 2>;
 constexpr int kStagePad = 16;
 
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
       b_src.base[i] = W;
       b_src.off[i] = (uint32_t)(kr * p.N * 2) + kload_col<TL::BN>(kr, lane);
     }
-    mainloop_t<TL, false, true>(a_src, b_src, p.K / TL::BK, lds, acc, TL::RB, (int64_t)64 * p.N * 2);
+    mainloop<TL, true, false, true>(a_src, b_src, p.K / TL::BK, lds, acc, TL::RB, (int64_t)64 * p.N * 2);
   }
   constexpr int ld = TL::BN * 2 + kStagePad;
   constexpr int cpr = TL::BN * 2 / 16;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(WgradTile::THREADS) void wgrad_kernel(BwdWgrad p) {
   }
   Acc<TL> acc;
   acc.zero();
-  mainloop_t<TL, true, true>(a_src, b_src, ktiles, lds, acc, 64 * p.x_row_bytes, 64 * p.y_row_bytes);
+  mainloop<TL, false, true, true>(a_src, b_src, ktiles, lds, acc, 64 * p.x_row_bytes, 64 * p.y_row_bytes);
   constexpr int ld = TL::BN * 2 + kStagePad;
   stage<TL>(acc, lds, ld, 0);
   __syncthreads();

@@ -167,16 +167,105 @@ struct Frags {
   uint4 b[TL::NI];
 };
 
-template <class TL>
+// ---- K-major operands --------------------------------------------------
+// The backward of the routed experts contracts weights along their output
+// dimension (dgrad) and activations along their rows (wgrad): such an
+// operand is stored K-major, rows along K with the M (or N) index
+// contiguous.  Its K tile is staged in LDS as it lies in memory, 64 k-rows
+// of X bf16, and turned into MFMA fragments on the way out of LDS by
+// ds_read_b64_tr_b16, which transposes 16-bit elements across the lanes of
+// each group of 16.
+//
+// Lane layout of ds_read_b64_tr_b16 (read off the device with an in-bounds
+// probe): within each group of 16 lanes, lane i receives, as its 4 results
+// j = 0..3, element (i & 3) of the 4 consecutive elements addressed by lane
+// 4 j + (i >> 2) of its group.  So if lane 4 j + q of group g addresses k-row
+// 8 g + 4 h + j at column x0 + 4 q, lane i gets column x0 + i of k-rows
+// 8 g + 4 h + 0..3: two such reads (h = 0, 1) give the 8 consecutive k of
+// one v_mfma_f32_16x16x32_bf16 operand row, the registers a row-major
+// fragment read yields.
+//
+// LDS layout of a K-major tile: k-row k at k * 2X bytes, its 16-byte chunks
+// XOR-swizzled by swz(k), so that the 16 k-rows one read touches land on
+// distinct chunk positions (2 LDS cycles per read at 256 bytes a cycle; the
+// profiled SQ_LDS_BANK_CONFLICT is 0).
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+template <int X>
+struct KMajor {
+  static_assert(X == 128 || X == 256, "K-major tiles are 128 or 256 wide");
+  static constexpr int RB = 2 * X;        // bytes per k-row
+  static constexpr int CPR = RB / 16;     // 16-byte chunks per k-row
+  static constexpr int RPI = 1024 / RB;   // k-rows per load instruction
+  // distinct over k & 3 and bits 3.. of k for the 16 k-rows 8 g + 4 h + j
+  // (g < 4, j < 4) of one transposed read
+  __device__ __forceinline__ static int swz(int k) {
+    return X == 256 ? (((k & 3) | (((k >> 3) & 3) << 2)) << 1) : (((k & 3) | (((k >> 3) & 1) << 2)) << 1);
+  }
+};
+
+// K-row that lane `lane` of wavefront `wave` loads with instruction i, and
+// the byte offset of the logical chunk it fetches (its LDS slot is 16 lane).
+template <class TL, int X>
+__device__ __forceinline__ int kload_row(int i, int wave, int lane) {
+  return (i * TL::NW + wave) * KMajor<X>::RPI + lane / KMajor<X>::CPR;
+}
+template <int X>
+__device__ __forceinline__ int kload_col(int krow, int lane) {
+  return ((lane % KMajor<X>::CPR) ^ KMajor<X>::swz(krow)) << 4;
+}
+
+// One MFMA operand (16 columns from xb, K sub-step ks of 32) of a K-major
+// tile at st.
+template <int X>
+__device__ __forceinline__ uint4 kfrag(const char* st, int xb, int ks, int lane) {
+  const int g = (lane >> 4) & 3, j = (lane >> 2) & 3, q = lane & 3;
+  const int sw = KMajor<X>::swz(8 * g + j);  // the same for both halves and every ks
+  const int c = ((xb >> 3) + (q >> 1)) ^ sw;
+  const char* p = st + (ks * 32 + 8 * g + j) * KMajor<X>::RB + (c << 4) + (q & 1) * 8;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)p);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * KMajor<X>::RB));
+  const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+  return make_uint4(l.x, l.y, h.x, h.y);
+}
+
+// Fragment r of sub-step ks (r < MI: A block r; else B block r - MI), each
+// operand row-major (the Tile layout) or K-major (AK / BK; X = BM or BN).
+template <class TL, bool AK, bool BK>
+__device__ __forceinline__ uint4 frag(const char* sa, const char* sb, int ks, int r, int wm, int wn, int lane) {
+  const int off = ((ks * 4 + (lane >> 4)) ^ TL::swz(lane & 15)) << 4;
+  if (r < TL::MI) {
+    if constexpr (AK) return kfrag<TL::BM>(sa, wm * TL::WM + r * 16, ks, lane);
+    return ld16(sa + (wm * TL::WM + (lane & 15)) * TL::RB + r * 16 * TL::RB + off);
+  }
+  const int n = r - TL::MI;
+  if constexpr (BK) return kfrag<TL::BN>(sb, wn * TL::WN + n * 16, ks, lane);
+  return ld16(sb + (wn * TL::WN + (lane & 15)) * TL::RB + n * 16 * TL::RB + off);
+}
+
+// LDS read instructions of one sub-step's fragments (a K-major one takes two).
+template <class TL, bool AK, bool BK>
+constexpr int frag_reads() {
+  return (AK ? 2 : 1) * TL::MI + (BK ? 2 : 1) * TL::NI;
+}
+
+template <class TL, bool AK = false, bool BK = false>
 __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int ks, Frags<TL>& f, int wm, int wn,
                                            int lane) {
-  const char* a = sa + (wm * TL::WM + (lane & 15)) * TL::RB;
-  const char* b = sb + (wn * TL::WN + (lane & 15)) * TL::RB;
-  const int off = ((ks * 4 + (lane >> 4)) ^ TL::swz(lane & 15)) << 4;
+  if constexpr (!AK && !BK) {
+    const char* a = sa + (wm * TL::WM + (lane & 15)) * TL::RB;
+    const char* b = sb + (wn * TL::WN + (lane & 15)) * TL::RB;
+    const int off = ((ks * 4 + (lane >> 4)) ^ TL::swz(lane & 15)) << 4;
 #pragma unroll
-  for (int mi = 0; mi < TL::MI; ++mi) f.a[mi] = ld16(a + mi * 16 * TL::RB + off);
+    for (int mi = 0; mi < TL::MI; ++mi) f.a[mi] = ld16(a + mi * 16 * TL::RB + off);
 #pragma unroll
-  for (int ni = 0; ni < TL::NI; ++ni) f.b[ni] = ld16(b + ni * 16 * TL::RB + off);
+    for (int ni = 0; ni < TL::NI; ++ni) f.b[ni] = ld16(b + ni * 16 * TL::RB + off);
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < TL::MI; ++mi) f.a[mi] = frag<TL, AK, BK>(sa, sb, ks, mi, wm, wn, lane);
+#pragma unroll
+    for (int ni = 0; ni < TL::NI; ++ni) f.b[ni] = frag<TL, AK, BK>(sa, sb, ks, TL::MI + ni, wm, wn, lane);
+  }
 }
 
 template <class TL>
@@ -191,12 +280,12 @@ __device__ __forceinline__ void mfma_frags(const Frags<TL>& f, Acc<TL>& acc) {
 
 // MFMAs on `cur` with the reads of `nxt` (sub-step ks of the staged tile at
 // sa, sb) interleaved among them.
-template <class TL>
+template <class TL, bool AK = false, bool BK = false>
 __device__ __forceinline__ void mfma_and_read(const Frags<TL>& cur, Acc<TL>& acc, const char* sa, const char* sb,
                                               int ks, Frags<TL>& nxt, int wm, int wn, int lane) {
-  read_frags<TL>(sa, sb, ks, nxt, wm, wn, lane);
+  read_frags<TL, AK, BK>(sa, sb, ks, nxt, wm, wn, lane);
   mfma_frags<TL>(cur, acc);
-  constexpr int NR = TL::MI + TL::NI;
+  constexpr int NR = frag_reads<TL, AK, BK>();
   constexpr int NM = TL::MI * TL::NI;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -213,23 +302,31 @@ __device__ __forceinline__ void mfma_and_read(const Frags<TL>& cur, Acc<TL>& acc
 // Each load sits between two fragment reads in program order (the inline
 // assembly is a memory barrier to the compiler), and the reads are
 // interleaved with the MFMAs.
-template <class TL, int P, class F>
+template <class TL, int P, bool AK = false, bool BK = false, class F>
 __device__ __forceinline__ void mfma_read_issue(const Frags<TL>& cur, Acc<TL>& acc, const char* sa, const char* sb,
                                                 int ks, Frags<TL>& nxt, int wm, int wn, int lane, F&& issue) {
-  constexpr int NR = TL::MI + TL::NI, NM = TL::MI * TL::NI;
+  constexpr int NF = TL::MI + TL::NI, NR = frag_reads<TL, AK, BK>(), NM = TL::MI * TL::NI;
   const char* a = sa + (wm * TL::WM + (lane & 15)) * TL::RB;
   const char* b = sb + (wn * TL::WN + (lane & 15)) * TL::RB;
   const int off = ((ks * 4 + (lane >> 4)) ^ TL::swz(lane & 15)) << 4;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    if (r < TL::MI)
-      nxt.a[r] = ld16(a + r * 16 * TL::RB + off);
-    else
-      nxt.b[r - TL::MI] = ld16(b + (r - TL::MI) * 16 * TL::RB + off);
-    // loads s with floor(s * NR / P) == r follow read r
+  for (int r = 0; r < NF; ++r) {
+    if constexpr (!AK && !BK) {
+      if (r < TL::MI)
+        nxt.a[r] = ld16(a + r * 16 * TL::RB + off);
+      else
+        nxt.b[r - TL::MI] = ld16(b + (r - TL::MI) * 16 * TL::RB + off);
+    } else {
+      const uint4 v = frag<TL, AK, BK>(sa, sb, ks, r, wm, wn, lane);
+      if (r < TL::MI)
+        nxt.a[r] = v;
+      else
+        nxt.b[r - TL::MI] = v;
+    }
+    // loads s with floor(s * NF / P) == r follow fragment r
 #pragma unroll
     for (int s = 0; s < P; ++s)
-      if (s * NR / P == r) issue(s);
+      if (s * NF / P == r) issue(s);
   }
   mfma_frags<TL>(cur, acc);
 #pragma unroll
@@ -266,7 +363,7 @@ __device__ __forceinline__ void wait_loads() {
 // kSplit selects the mid-tile barrier schedule (64-wide K tiles, 2 A
 // stages); it holds two fragment sets live, so kernels short of registers
 // take the plain schedule.
-template <class TL, bool kSplit = true>
+template <class TL, bool kSplit = true, bool AK = false, bool BK = false>
 __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const RowSrc<TL::B_INS>& b_src,
                                          int ktiles, char* lds,
                                          Acc<TL>& acc, int64_t a_kstep = TL::RB, int64_t b_kstep = TL::RB) {
@@ -301,7 +398,7 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
     else
       wait_loads<0>();
     Frags<TL> f0, f1;
-    read_frags<TL>(lds_a, lds_b, 0, f0, wm, wn, lane);
+    read_frags<TL, AK, BK>(lds_a, lds_b, 0, f0, wm, wn, lane);
     int sb = 0;  // B stage of tile kt
     int kt = 0;
     // every load of the iteration is in range: A(kt+2), B(kt+NSB), issued
@@ -310,7 +407,7 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
     for (; kt + TL::NSB < ktiles; ++kt) {
       int sb1 = sb + 1;
       if (sb1 == TL::NSB) sb1 = 0;
-      mfma_and_read<TL>(f0, acc, lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
+      mfma_and_read<TL, AK, BK>(f0, acc, lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
       // landed: A(kt+1), B(kt+1); may still fly: B(kt+2) when B runs 2 ahead
       if (DB == 2)
         wait_loads<PB>();
@@ -320,7 +417,7 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
       const int64_t ka = (kt + 2) * a_kstep, kb = (kt + TL::NSB) * b_kstep;
       char* da = lds_a + (kt & 1) * TL::A_BYTES + wave * 1024;
       char* db = lds_b + sb * TL::B_BYTES + wave * 1024;
-      mfma_read_issue<TL, TL::A_INS + TL::B_INS>(
+      mfma_read_issue<TL, TL::A_INS + TL::B_INS, AK, BK>(
           f1, acc, lds_a + ((kt + 1) & 1) * TL::A_BYTES, lds_b + sb1 * TL::B_BYTES, 0, f0, wm, wn, lane, [&](int s) {
             if (s < TL::A_INS)
               lds_load16(a_src.base[s] + ka, a_src.off[s], da + s * TL::NW * 1024);
@@ -334,7 +431,7 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
     for (; kt + 1 < ktiles; ++kt) {
       int sb1 = sb + 1;
       if (sb1 == TL::NSB) sb1 = 0;
-      mfma_and_read<TL>(f0, acc, lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
+      mfma_and_read<TL, AK, BK>(f0, acc, lds_a + (kt & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
       if (DB == 2 && kt + 2 < ktiles)
         wait_loads<PB>();
       else
@@ -342,14 +439,49 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
       if (kt + 2 < ktiles) issue_rows<TL>(a_src, (kt + 2) * a_kstep, lds_a + (kt & 1) * TL::A_BYTES, wave);
       if (kt + TL::NSB < ktiles)
         issue_rows<TL>(b_src, (kt + TL::NSB) * b_kstep, lds_b + sb * TL::B_BYTES, wave);
-      mfma_and_read<TL>(f1, acc, lds_a + ((kt + 1) & 1) * TL::A_BYTES, lds_b + sb1 * TL::B_BYTES, 0, f0, wm, wn,
+      mfma_and_read<TL, AK, BK>(f1, acc, lds_a + ((kt + 1) & 1) * TL::A_BYTES, lds_b + sb1 * TL::B_BYTES, 0, f0, wm, wn,
                         lane);
       sb = sb1;
     }
     const int kl = ktiles - 1;
-    mfma_and_read<TL>(f0, acc, lds_a + (kl & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
+    mfma_and_read<TL, AK, BK>(f0, acc, lds_a + (kl & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
     mfma_frags<TL>(f1, acc);
+  } else if constexpr ((AK || BK) && TL::NSB == TL::NS && TL::NS == 2 && TL::KS == 2) {
+    // K-major operands on the plain schedule: the loads of tile kt + 1
+    // after the barrier that frees its stage, then tile kt's MFMAs with the
+    // second half's fragment reads interleaved (fewer live registers than
+    // the split schedule, whose two fragment sets would spill here)
+    if (ktiles > 0) {
+      issue_rows<TL>(a_src, 0, lds_a, wave);
+      issue_rows<TL>(b_src, 0, lds_b, wave);
+    }
+    for (int kt = 0; kt < ktiles; ++kt) {
+      wait_loads<0>();
+      const int st = kt & 1;
+      if (kt + 1 < ktiles) {
+        issue_rows<TL>(a_src, (kt + 1) * a_kstep, lds_a + (st ^ 1) * TL::A_BYTES, wave);
+        issue_rows<TL>(b_src, (kt + 1) * b_kstep, lds_b + (st ^ 1) * TL::B_BYTES, wave);
+      }
+      const char* sa = lds_a + st * TL::A_BYTES;
+      const char* sb = lds_b + st * TL::B_BYTES;
+      Frags<TL> f0, f1;
+      read_frags<TL, AK, BK>(sa, sb, 0, f0, wm, wn, lane);
+      read_frags<TL, AK, BK>(sa, sb, 1, f1, wm, wn, lane);
+      mfma_frags<TL>(f0, acc);
+      mfma_frags<TL>(f1, acc);
+      constexpr int NR = frag_reads<TL, AK, BK>();
+      constexpr int NM = TL::MI * TL::NI;
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    }
   } else if constexpr (TL::NSB == TL::NS) {
+    static_assert(!AK && !BK, "K-major operands: split schedule, or the plain one with 2 stages");
 #pragma unroll
     for (int s = 0; s < TL::NS - 1; ++s)
       if (s < ktiles) {
@@ -409,6 +541,7 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
       if (++stage == TL::NS) stage = 0;
     }
   } else {
+    static_assert(!AK && !BK, "K-major operands: split schedule, or the plain one with 2 stages");
     // 2 A stages (A one tile ahead), NSB B stages (B DB = NSB - 1 tiles
     // ahead).  Issue order: B0 A0 B1 .. B(DB-1) | A1 B(DB) | A2 B(DB+1) | ...
     // At the top of iteration kt >= 1 the last loads issued are A(kt) then
