@@ -223,3 +223,95 @@ def test_dropped_rows_sent_back_is_caught(monkeypatch):
                 np.asarray(gate_w, dtype=np.float64)[:, :, None] * dy[:, None, :])
     monkeypatch.setattr(ob, "combine_backward", wrong_combine)
     assert _fails(tb.test_dropped_assignments_get_nothing)
+
+
+# --------------------------------------------------------------- router bias
+import oracle.router_bias as rbm
+import test_oracle_bias as tbias
+
+_BIAS_PINS = [tbias.test_worked_example_by_hand, tbias.test_rank_on_a_bin_edge_takes_that_bin,
+              tbias.test_rank_before_an_empty_bin_is_the_generalised_inverse,
+              lambda: tbias.test_quantile_inverts_the_interpolated_cdf(4096, 16, 2, 16),
+              tbias.test_histogram_matches_numpy_on_exact_edges, tbias.test_quantile_within_one_bin_of_the_sample_quantile,
+              tbias.test_shift_equivariance_is_exact, tbias.test_zero_mean, tbias.test_special_levels,
+              tbias.test_the_bias_balances_a_skewed_router]
+
+
+def _some_bias_pin_fails():
+    return any(_fails(f) for f in _BIAS_PINS)
+
+
+def _quantile_variant(level_of=None, strict=False, width_div=0):
+    def q(hist, lo, hi, T, top_k):
+        hist = np.asarray(hist, dtype=np.int64)
+        E, nb = hist.shape
+        level = level_of(E, top_k) if level_of else Fraction(E - top_k, E)
+        r = float(level * T)
+        out = np.empty(E)
+        for e in range(E):
+            c = np.cumsum(hist[e])
+            j = int(np.argmax(c > r)) if strict else int(np.argmax(c >= r))
+            cp = int(c[j - 1]) if j > 0 else 0
+            w = (float(hi[e]) - float(lo[e])) / (nb - width_div if nb > width_div else 1)
+            out[e] = float(lo[e]) + (j + (r - cp) / int(hist[e, j])) * w
+        return out
+    return q
+
+
+def test_bias_pins_pass_on_the_real_oracle():
+    assert not _some_bias_pin_fails()
+
+
+def test_lower_tail_level_is_caught(monkeypatch):
+    monkeypatch.setattr(rbm, "histogram_quantile", _quantile_variant(level_of=lambda E, k: Fraction(k, E)))
+    assert _some_bias_pin_fails()
+
+
+def test_strict_rank_search_is_caught(monkeypatch):
+    monkeypatch.setattr(rbm, "histogram_quantile", _quantile_variant(strict=True))
+    assert _some_bias_pin_fails()
+
+
+def test_bin_width_off_by_one_is_caught(monkeypatch):
+    monkeypatch.setattr(rbm, "histogram_quantile", _quantile_variant(width_div=1))
+    assert _some_bias_pin_fails()
+
+
+def test_missing_mean_removal_is_caught(monkeypatch):
+    def no_centre(logits32, top_k, n_bins):
+        l = np.asarray(logits32, dtype=np.float32)
+        hist, lo, hi = rbm.histograms(l, n_bins)
+        q = rbm.histogram_quantile(hist, lo, hi, l.shape[0], top_k)
+        return (-q).astype(np.float32), hist, lo, hi, q
+    monkeypatch.setattr(rbm, "bias_update", no_centre)
+    monkeypatch.setattr(tbias.rb, "bias_update", no_centre)
+    assert _some_bias_pin_fails()
+
+
+def test_bias_sign_flip_is_caught(monkeypatch):
+    real = rbm.bias_update
+
+    def flipped(logits32, top_k, n_bins):
+        b, *rest = real(logits32, top_k, n_bins)
+        return (-b).astype(np.float32), *rest
+    monkeypatch.setattr(tbias.rb, "bias_update", flipped)
+    assert _some_bias_pin_fails()
+
+
+def test_global_range_instead_of_per_expert_is_caught(monkeypatch):
+    real_range = rbm.logit_range
+
+    def global_range(logits32):
+        lo, hi = real_range(logits32)
+        return np.full_like(lo, lo.min()), np.full_like(hi, hi.max())
+    monkeypatch.setattr(rbm, "logit_range", global_range)
+    assert _some_bias_pin_fails()
+
+
+def test_round_to_nearest_bin_is_caught(monkeypatch):
+    def nearest(logits32, lo, scale, n_bins):
+        l = np.asarray(logits32, dtype=np.float32)
+        p = ((l - lo[None, :]) * scale[None, :]).astype(np.float32)
+        return np.minimum(np.rint(p).astype(np.int64), n_bins - 1)
+    monkeypatch.setattr(rbm, "bin_index", nearest)
+    assert _some_bias_pin_fails()
