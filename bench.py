@@ -10,7 +10,8 @@ already resident in HBM.  Prints one JSON line.  --dropless times the
 dropless ragged variant; --backward times the routed path's backward
 (moe_backward_routed, or moe_backward_dropless with --dropless: gate, row and
 weight gradients for one forward call's routing, a seeded dL/dy_latent,
-forward state resident).
+forward state resident); --bias-update times the router's next-step bias
+update (moe_router_bias_update) on one forward call's logits.
 
 Stage durations come from HIP events the library records between its kernel
 launches on the stream it launches them on (moe_forward_profiled), averaged
@@ -32,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; % bf16 MFMA peak; drop fraction"
 METRIC_BWD = "MoE routed-path bwd tokens/sec on 1 MI355X; % bf16 MFMA peak"
+METRIC_BIAS = "MoE router next-step bias update tokens/sec on 1 MI355X; % HBM peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 
@@ -48,19 +50,23 @@ STAGE_KERNEL = {
     "dh": ("dgrad_kernel", "<0>"),
     "du": ("dgrad_kernel", "<1>"),
     "dw_down": ("wgrad_kernel",),
+    "bias_range": ("range_kernel",),
+    "bias_hist": ("hist_kernel",),
+    "bias_quantile": ("quantile_kernel",),
 }
 COPY_KERNEL = ("copyBuffer",)
 # sources of the GEMM kernels: a measured traffic figure is used only while
 # they are unchanged
 KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "dispatch.hip",
                   "gemm_bwd.hip", "backward.hip"]
+BIAS_SOURCES = ["bias.hip", "common.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(run_name=""):
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "routing_capacity_dispatch_amd", "csrc")
-    for f in KERNEL_SOURCES:
+    for f in (BIAS_SOURCES if run_name.endswith("_bias") else KERNEL_SOURCES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -98,17 +104,26 @@ def summarize_pmc(fetch_csv, write_csv, stage, workload, copy_bytes, out_path, c
            "copy_bytes": copy_bytes, "copy_fetch_kib": fc, "copy_write_kib": wc,
            "fetch_scale": f_scale, "write_scale": w_scale,
            "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale,
-           "source_sha256": kernel_source_hash(), "command": command}
+           "source_sha256": kernel_source_hash(workload), "command": command}
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
 
-def stage_work(w, kept, sent, dropless=False, backward=False):
+def stage_work(w, kept, sent, dropless=False, backward=False, bias_bins=0):
     """Algorithmic flops (MFMA stages) or bytes (HBM stages) per launch."""
     eb = 2 if w.dtype == "bf16" else 4
     T, D, L, E, k, F = w.T, w.d_model, w.d_latent, w.n_experts, w.top_k, w.d_ff
     S, Fs = w.n_shared, w.d_ff_shared
+    if bias_bins:
+        # each pass over the fp32 logits reads them once; the histogram and
+        # the quantiles are read or written once
+        return {
+            "bias_range": ("hbm", T * E * 4),
+            "bias_hist": ("hbm", T * E * 4),
+            "bias_quantile": ("hbm", E * bias_bins * 4 + E * 8),
+            "bias_mean": ("hbm", E * 12),
+        }
     if backward:
         # kept rows only, never the 64-row padding of the expert layout
         return {
@@ -153,6 +168,25 @@ def stage_work(w, kept, sent, dropless=False, backward=False):
         "shared_gate_up": ("mfma", 2.0 * T * D * 2 * S * Fs),
         "output": ("mfma", 2.0 * T * D * (L + S * Fs)),
     }
+
+
+def cpu_baseline_bias(logits, top_k, n_bins):
+    """The oracle's bias update on the whole step's logits (numpy, one core)."""
+    from oracle import router_bias
+
+    l = logits.detach().cpu().numpy()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        b = router_bias.bias_update(l, top_k, n_bins)[0]
+        n += 1
+        if time.perf_counter() - t0 > 5.0:
+            break
+    dt = (time.perf_counter() - t0) / n
+    assert b.shape == (l.shape[1],)
+    return {"value": l.shape[0] / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole step's {l.shape[0]}x{l.shape[1]} fp32 logits, {n_bins} bins, "
+                      f"{n} oracle calls of {dt:.2f} s (numpy, single-threaded)"}
 
 
 def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
@@ -226,6 +260,10 @@ def main():
                     help="time the dropless ragged variant (moe_forward_dropless) instead")
     ap.add_argument("--backward", action="store_true",
                     help="time the routed path's backward (moe_backward_routed) instead")
+    ap.add_argument("--bias-update", action="store_true",
+                    help="time the router's next-step bias update (moe_router_bias_update) on one "
+                         "forward call's logits instead")
+    ap.add_argument("--bins", type=int, default=256, help="histogram bins of --bias-update")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="oracle sample for the CPU baseline (default 256; 64 with --backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -241,7 +279,8 @@ def main():
     ap.add_argument("--stage", default="expert_gate_up", help="stage for --summarize-pmc")
     ap.add_argument("--pmc-command", default="", help="command recorded by --summarize-pmc")
     args = ap.parse_args()
-    run_name = args.workload + ("_dropless" if args.dropless else "") + ("_backward" if args.backward else "")
+    run_name = (args.workload + ("_dropless" if args.dropless else "") + ("_backward" if args.backward else "")
+                + ("_bias" if args.bias_update else ""))
     if args.cpu_tokens is None:
         args.cpu_tokens = 64 if args.backward else 256
     if args.traffic is None:
@@ -273,7 +312,13 @@ def main():
     x = inp["x"]
     weights = {k: v for k, v in inp.items() if k != "x"}
     dy = None
-    if args.backward:
+    if args.bias_update:
+        fwd = rcd.Forward(cfg, weights, dev, taps=True)
+        fwd(x)           # the step whose router logits feed the update
+        step = rcd.RouterBias(cfg, args.bins, dev)
+        nst = rcd.router_bias_stage_count()
+        stages = rcd.abi.BIAS_STAGES
+    elif args.backward:
         fwd = (rcd.ForwardDropless if args.dropless else rcd.Forward)(cfg, weights, dev, taps=True)
         fwd(x)           # the forward call whose gradient is taken: state saved
         dy = synth.grad_latent(w, args.seed, device=dev)
@@ -290,7 +335,7 @@ def main():
         nst = rcd.stage_count()
         stages = rcd.abi.STAGES
         step = fwd
-    arg = dy if args.backward else x
+    arg = dy if args.backward else (fwd.tap_t["logits"] if args.bias_update else x)
     if args.calib_copy_mb:
         n = args.calib_copy_mb * 1024 * 1024
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -329,7 +374,8 @@ def main():
             per[s] += ev[i][j].elapsed_time(ev[i][j + 1]) / K
     kept, sd, rd = [int(v) for v in fwd.counts.cpu().tolist()]
     sent = kept + rd
-    work = stage_work(w, kept, sent, dropless=args.dropless and not args.backward, backward=args.backward)
+    work = stage_work(w, kept, sent, dropless=args.dropless and not args.backward, backward=args.backward,
+                      bias_bins=args.bins if args.bias_update else 0)
     peak_f = PEAK_TFLOPS[w.dtype]
     st_out = {}
     for s in stages:
@@ -359,15 +405,16 @@ def main():
         try:
             tr = json.load(open(args.traffic))
             if (tr.get("stage") == dom and tr.get("workload") == run_name
-                    and tr.get("source_sha256") == kernel_source_hash()):
+                    and tr.get("source_sha256") == kernel_source_hash(run_name)):
                 roof["traffic"] = round(tr["bytes_per_launch"])
         except (OSError, ValueError, KeyError):
             pass
     gemm_flops = sum(work[s][1] for s in stages if work[s][0] == "mfma")
     gemm_ms = sum(per[s] for s in stages if work[s][0] == "mfma")
+    pass_name = "router_bias" if args.bias_update else ("backward" if args.backward else "forward")
     tokens_s = w.T / (ms_step * 1e-3)
     out = {
-        "metric": METRIC_BWD if args.backward else METRIC,
+        "metric": METRIC_BIAS if args.bias_update else (METRIC_BWD if args.backward else METRIC),
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -377,21 +424,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "f32" if args.bias_update else w.dtype,
         "data": "synthetic",
-        "config": {"workload": run_name, "pass": "backward" if args.backward else "forward", "T": w.T, "d_model": w.d_model, "d_latent": w.d_latent,
+        "config": {"workload": run_name, "pass": pass_name, "T": w.T, "d_model": w.d_model, "d_latent": w.d_latent,
                    "n_experts": w.n_experts, "n_pools": w.n_pools, "top_k": w.top_k,
                    "d_ff": w.d_ff, "n_shared": w.n_shared, "d_ff_shared": w.d_ff_shared,
                    "n_waves": w.n_waves, "caps": [list(w.send_cap), list(w.recv_cap)],
                    "global_batch": w.T, "parallelism": "single GPU"},
         "roofline": roof,
-        "gemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_f, 4),
+        "gemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_f, 4) if gemm_ms > 0 else None,
         "drop_fraction": {"sender": sd / (w.T * w.top_k), "receiver": rd / (w.T * w.top_k),
                           "total": (sd + rd) / (w.T * w.top_k)},
         "stages": st_out,
         "wall_s_timed": round(wall, 3),
     }
-    if not args.no_cpu_baseline:
+    if args.bias_update:
+        out["config"]["bins"] = args.bins
+    if not args.no_cpu_baseline and args.bias_update:
+        print("# cpu baseline: oracle bias update", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_bias(arg, w.top_k, args.bins)
+    elif not args.no_cpu_baseline:
         print(f"# cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, dropless=args.dropless,
                                            backward=args.backward, dy_latent=dy)

@@ -182,6 +182,53 @@ moe_status moe_route(const moe_config* cfg, const float* logits,
                      const float* bias, int32_t* topk_idx, float* gates,
                      void* stream);
 
+/* Router balancing-bias update (ranhao.site section 2.2: the top-8 router
+   is a histogram-based quantile router; its bias is zero-mean, computed for
+   the next step, a heuristic that balances expert selection, outside the
+   gradient).  The page gives no formula; the rule computed here is:
+     1. per expert e, lo_e / hi_e = min / max of its logit over the T tokens;
+     2. an n_bins equal-width histogram of the column over [lo_e, hi_e]: the
+        bin of v is 0 if v == lo_e, else min(n_bins - 1, trunc(p)) with
+        p = fl32(fl32(v - lo_e) * scale_e), scale_e = fl32 of the fp64
+        quotient n_bins / (hi_e - lo_e) (0 for a constant column);
+     3. Q_e = the quantile of level 1 - k/E read off the histogram by linear
+        interpolation inside the first bin j whose cumulative count C_j
+        satisfies C_j * E >= (E - k) * T:
+          Q_e = lo_e + (j + (r - C_{j-1}) / h_j) * (hi_e - lo_e) / n_bins,
+        r = (E - k) * T / E, each operation rounded in fp64;
+     4. bias_next[e] = mean(Q) - Q_e, rounded to fp32 (zero-mean).
+   Adding bias_next to the next step's logits before top-k moves every
+   expert's 1 - k/E quantile onto the common mean, so each expert's logit
+   clears a common threshold on about a k/E share of the tokens.
+   logits    (device) [T][E] fp32, finite; ranges narrower than about
+             n_bins * 2^-126 meet fp32 denormals and are not supported
+   n_bins    1 <= n_bins <= 1024
+   bias_next (device, out) [E] fp32
+   hist      (device, out) [E][n_bins] int32 counts, or NULL
+   lohi      (device, out) [E][2] fp32 {lo_e, hi_e}, or NULL
+   ws        (device) >= moe_router_bias_ws_bytes(cfg, n_bins) bytes,
+             256-byte aligned; nothing in it needs clearing.  Calls that
+             share a workspace must not overlap (one stream does that)
+   Only T, n_experts and top_k of *cfg are read: T >= 1 and 1 <= top_k <=
+   n_experts (MOE_ERR_INVALID_ARG), n_experts <= 1024 (MOE_ERR_UNSUPPORTED).
+   Null logits or bias_next: MOE_ERR_INVALID_ARG; a null, misaligned or
+   short workspace: MOE_ERR_WORKSPACE.
+   The result is bitwise reproducible: counts are integers and every sum has
+   a fixed order. */
+moe_status moe_router_bias_ws_bytes(const moe_config* cfg, int32_t n_bins, size_t* bytes);
+moe_status moe_router_bias_update(const moe_config* cfg, const float* logits, int32_t n_bins,
+                                  float* bias_next, int32_t* hist, float* lohi, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* moe_router_bias_update recording stage_events (n_events >= 5 hipEvent_t,
+   created by the caller) on the stream around its 4 launches: 0 per-chunk
+   ranges, 1 per-chunk histograms, 2 quantiles, 3 the mean and the bias. */
+int32_t moe_router_bias_stage_count(void);
+moe_status moe_router_bias_update_profiled(const moe_config* cfg, const float* logits,
+                                           int32_t n_bins, float* bias_next, int32_t* hist,
+                                           float* lohi, void* ws, size_t ws_bytes, void* stream,
+                                           void* const* stage_events, int32_t n_events);
+
 /* Sender pooling and receiver binning (lamjinlab.com section 2: one fixed
    pool per receiving destination rather than one buffer per expert, three
    waves of identical array shapes, expert ids packed into the payload,

@@ -1,5 +1,6 @@
 """fp64 CPU oracle of the pooled-wave capacity-dispatch MoE forward and of
-the backward of its routed path.
+the backward of its routed path, and of the router's next-step bias update
+(`oracle.router_bias`).
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path.  Every function is

@@ -54,23 +54,30 @@ def bin_scale(lo, hi, n_bins):
     """scale_e = fl32(n_bins / (hi_e - lo_e)), 0 for a constant column.
 
     The difference of two fp32 values is exact in fp64; the quotient is
-    rounded to fp64 and then to fp32."""
+    rounded to fp64 and then to fp32 (inf when a range is narrower than
+    n_bins / FLT_MAX)."""
     lo64 = np.asarray(lo, dtype=np.float32).astype(np.float64)
     hi64 = np.asarray(hi, dtype=np.float32).astype(np.float64)
     width = hi64 - lo64
     out = np.zeros_like(width)
     nz = width > 0
     out[nz] = float(n_bins) / width[nz]
-    return out.astype(np.float32)
+    with np.errstate(over="ignore"):
+        return out.astype(np.float32)
 
 
 def bin_index(logits32, lo, scale, n_bins):
-    """bin[t, e] = min(n_bins - 1, trunc(fl32(fl32(v - lo_e) * scale_e)))."""
+    """bin[t, e] = min(n_bins - 1, trunc(fl32(fl32(v - lo_e) * scale_e))).
+
+    v >= lo_e, so the product is >= 0 and truncation is the floor; a value
+    equal to lo_e is in bin 0 whatever the scale (also an infinite one)."""
     l = np.asarray(logits32, dtype=np.float32)
     d = (l - np.asarray(lo, dtype=np.float32)[None, :]).astype(np.float32)
-    p = (d * np.asarray(scale, dtype=np.float32)[None, :]).astype(np.float32)
-    # v >= lo_e, so d >= 0 and p >= 0: truncation is the floor
-    return np.minimum(p.astype(np.int64), n_bins - 1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = (d * np.asarray(scale, dtype=np.float32)[None, :]).astype(np.float32)
+    b = np.where(p >= n_bins, np.float32(n_bins - 1), p)
+    b = np.where(d == 0, np.float32(0), b)
+    return b.astype(np.int64)
 
 
 def histograms(logits32, n_bins):

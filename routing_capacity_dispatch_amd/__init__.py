@@ -89,6 +89,54 @@ def route(cfg, logits: torch.Tensor, bias: Optional[torch.Tensor] = None, out=No
     return topk, gates
 
 
+def router_bias_ws_bytes(cfg, n_bins: int) -> int:
+    n = C.c_size_t(0)
+    abi.check("moe_router_bias_ws_bytes", library().moe_router_bias_ws_bytes(C.byref(cfg), n_bins, C.byref(n)))
+    return int(n.value)
+
+
+def router_bias_update(cfg, logits: torch.Tensor, n_bins: int, with_hist: bool = False, ws=None, out=None):
+    """Next step's zero-mean router bias [E] fp32 from this step's logits
+    [T][E] fp32 (moe_router_bias_update).  With with_hist, also the
+    per-expert counts [E][n_bins] int32 and ranges [E][2] fp32."""
+    dev = logits.device
+    E = cfg.n_experts
+    bias = out if out is not None else torch.empty(E, dtype=torch.float32, device=dev)
+    hist = torch.empty((E, n_bins), dtype=torch.int32, device=dev) if with_hist else None
+    lohi = torch.empty((E, 2), dtype=torch.float32, device=dev) if with_hist else None
+    if ws is None:
+        ws = _ws(router_bias_ws_bytes(cfg, n_bins), dev)
+    abi.check("moe_router_bias_update", library().moe_router_bias_update(
+        C.byref(cfg), _ptr(logits), n_bins, _ptr(bias), _ptr(hist), _ptr(lohi), _ptr(ws), ws.numel(),
+        _stream(dev)))
+    return (bias, hist, lohi) if with_hist else bias
+
+
+class RouterBias:
+    """moe_router_bias_update with its workspace and output allocated once:
+    call it with each step's logits [T][E] fp32; it returns the next step's
+    bias [E] fp32 (the same tensor every call)."""
+
+    def __init__(self, cfg, n_bins: int, device):
+        self.cfg, self.n_bins = cfg, n_bins
+        self.ws = _ws(router_bias_ws_bytes(cfg, n_bins), device)
+        self.bias = torch.empty(cfg.n_experts, dtype=torch.float32, device=device)
+
+    def __call__(self, logits: torch.Tensor):
+        return router_bias_update(self.cfg, logits, self.n_bins, ws=self.ws, out=self.bias)
+
+    def profiled(self, logits: torch.Tensor, events):
+        arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+        abi.check("moe_router_bias_update_profiled", library().moe_router_bias_update_profiled(
+            C.byref(self.cfg), _ptr(logits), self.n_bins, _ptr(self.bias), None, None, _ptr(self.ws),
+            self.ws.numel(), _stream(logits.device), arr, len(events)))
+        return self.bias
+
+
+def router_bias_stage_count() -> int:
+    return library().moe_router_bias_stage_count()
+
+
 def dispatch(cfg, topk_idx: torch.Tensor, z: torch.Tensor) -> Dict[str, torch.Tensor]:
     p = plan(cfg)
     dev = z.device

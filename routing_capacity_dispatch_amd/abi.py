@@ -69,6 +69,12 @@ SIGNATURES = {
     "moe_version": (C.c_int32, []),
     "moe_make_plan": (C.c_int, [C.POINTER(MoeConfig), C.POINTER(MoePlan)]),
     "moe_route": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P]),
+    "moe_router_bias_ws_bytes": (C.c_int, [C.POINTER(MoeConfig), C.c_int32, C.POINTER(C.c_size_t)]),
+    "moe_router_bias_update": (C.c_int, [C.POINTER(MoeConfig), _P, C.c_int32, _P, _P, _P, _P,
+                                         C.c_size_t, _P]),
+    "moe_router_bias_stage_count": (C.c_int32, []),
+    "moe_router_bias_update_profiled": (C.c_int, [C.POINTER(MoeConfig), _P, C.c_int32, _P, _P, _P, _P,
+                                                  C.c_size_t, _P, _P, C.c_int32]),
     "moe_dispatch": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, C.c_size_t, _P]),
     "moe_experts": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P,
@@ -122,6 +128,7 @@ STAGES = ["latent", "router", "topk", "assign", "scatter", "recv_bin", "expert_r
           "expert_gate_up", "expert_down", "combine", "shared_gate_up", "output"]
 DROPLESS_STAGES = ["latent", "router", "topk", "sort", "scatter", "tiles", "expert_gate_up",
                    "expert_down", "combine", "shared_gate_up", "output"]
+BIAS_STAGES = ["bias_range", "bias_hist", "bias_quantile", "bias_mean"]
 BACKWARD_STAGES = ["combine_bwd", "layout", "gather", "dh", "swiglu_bwd", "du", "dw_down",
                    "dw_gate", "dw_up", "dispatch_bwd", "route_bwd"]
 

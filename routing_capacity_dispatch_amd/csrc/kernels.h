@@ -75,6 +75,13 @@ hipError_t launch_swiglu_dense_bf16(const void* A, int64_t lda, const void* Wg, 
 hipError_t launch_topk_gates(const float* logits, const float* bias, int64_t T, int E,
                              int k, int32_t* topk_idx, float* gates, hipStream_t s);
 
+// Next-step balancing bias from histogram quantiles of the logits (bias.hip).
+int bias_max_bins();
+int64_t bias_ws_bytes(int64_t T, int E, int nb);
+// events: null, or 5 hipEvent_t recorded around the 4 launches
+hipError_t launch_bias_update(const float* logits, int64_t T, int E, int k, int nb, float* bias, int32_t* hist_out,
+                              float* lohi_out, void* ws, hipStream_t s, void* const* events);
+
 // ---------------------------------------------------------------- dispatch
 struct DispatchArgs {
   const int32_t* topk;

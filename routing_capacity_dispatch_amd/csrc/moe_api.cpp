@@ -473,6 +473,50 @@ MOE_API moe_status moe_route(const moe_config* cfg, const float* logits, const f
                                            topk_idx, gates, static_cast<hipStream_t>(stream)));
 }
 
+static moe_status check_bias_update(const moe_config* cfg, int32_t n_bins) {
+  moe_status st = check_route_shape(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T < 1 || cfg->top_k > cfg->n_experts) return MOE_ERR_INVALID_ARG;
+  if (n_bins < 1 || n_bins > moe::bias_max_bins()) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_router_bias_ws_bytes(const moe_config* cfg, int32_t n_bins, size_t* bytes) {
+  moe_status st = check_bias_update(cfg, n_bins);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = (size_t)moe::bias_ws_bytes(cfg->T, cfg->n_experts, n_bins);
+  return MOE_OK;
+}
+
+static moe_status bias_update_impl(const moe_config* cfg, const float* logits, int32_t n_bins, float* bias_next,
+                                   int32_t* hist, float* lohi, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* events) {
+  moe_status st = check_bias_update(cfg, n_bins);
+  if (st != MOE_OK) return st;
+  if (!logits || !bias_next) return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned256(ws) || (int64_t)ws_bytes < moe::bias_ws_bytes(cfg->T, cfg->n_experts, n_bins))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_bias_update(logits, cfg->T, cfg->n_experts, cfg->top_k, n_bins, bias_next, hist,
+                                            lohi, ws, static_cast<hipStream_t>(stream), events));
+}
+
+MOE_API moe_status moe_router_bias_update(const moe_config* cfg, const float* logits, int32_t n_bins,
+                                          float* bias_next, int32_t* hist, float* lohi, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  return bias_update_impl(cfg, logits, n_bins, bias_next, hist, lohi, ws, ws_bytes, stream, nullptr);
+}
+
+MOE_API int32_t moe_router_bias_stage_count(void) { return 4; }
+
+MOE_API moe_status moe_router_bias_update_profiled(const moe_config* cfg, const float* logits, int32_t n_bins,
+                                                   float* bias_next, int32_t* hist, float* lohi, void* ws,
+                                                   size_t ws_bytes, void* stream, void* const* stage_events,
+                                                   int32_t n_events) {
+  if (!stage_events || n_events < 5) return MOE_ERR_INVALID_ARG;
+  return bias_update_impl(cfg, logits, n_bins, bias_next, hist, lohi, ws, ws_bytes, stream, stage_events);
+}
+
 MOE_API moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const void* z,
                                 void* pools, int32_t* pool_slot, int32_t* recv_slot,
                                 int32_t* bank_rows, int32_t* pool_count, int32_t* expert_count,

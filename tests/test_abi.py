@@ -279,3 +279,39 @@ def test_dropless_backward_plan_and_validation(lib):
     assert lib.moe_backward_dropless(C.byref(bf), C.byref(ww), C.byref(taps), *([fake] * 6), fake,
                                      pb["dropless_backward_ws_bytes"], nul) == abi.MOE_ERR_INVALID_ARG
 
+
+
+def test_router_bias_update_validation(lib):
+    cfg = rcd.make_config(1000, 64, 64, 48, 8, 4, 64)
+    n = C.c_size_t(0)
+    assert lib.moe_router_bias_ws_bytes(C.byref(cfg), 256, C.byref(n)) == abi.MOE_OK
+    # range partials, per-chunk histograms, ranges and quantiles, each 256-aligned
+    c1, c2 = 1, 1
+    expect = sum((b + 255) // 256 * 256 for b in (c1 * 48 * 8, c2 * 48 * 256 * 4, 48 * 8, 48 * 8))
+    assert n.value == expect
+    for nb in (0, -1, 1025):
+        assert lib.moe_router_bias_ws_bytes(C.byref(cfg), nb, C.byref(n)) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_bias_ws_bytes(C.byref(cfg), 1024, C.byref(n)) == abi.MOE_OK
+    assert lib.moe_router_bias_ws_bytes(C.byref(cfg), 8, None) == abi.MOE_ERR_INVALID_ARG
+    fake, nul = C.c_void_p(0x100000), None
+    lib.moe_router_bias_ws_bytes(C.byref(cfg), 64, C.byref(n))
+    upd = lib.moe_router_bias_update
+    assert upd(C.byref(cfg), nul, 64, fake, nul, nul, fake, n.value, nul) == abi.MOE_ERR_INVALID_ARG
+    assert upd(C.byref(cfg), fake, 64, nul, nul, nul, fake, n.value, nul) == abi.MOE_ERR_INVALID_ARG
+    assert upd(C.byref(cfg), fake, 64, fake, nul, nul, nul, n.value, nul) == abi.MOE_ERR_WORKSPACE
+    assert upd(C.byref(cfg), fake, 64, fake, nul, nul, fake, n.value - 1, nul) == abi.MOE_ERR_WORKSPACE
+    assert upd(C.byref(cfg), fake, 64, fake, nul, nul, C.c_void_p(0x100080), n.value,
+               nul) == abi.MOE_ERR_WORKSPACE
+    bad = rcd.make_config(0, 64, 64, 48, 8, 4, 64)      # T = 0: no logits to take quantiles of
+    assert upd(C.byref(bad), fake, 64, fake, nul, nul, fake, n.value, nul) == abi.MOE_ERR_INVALID_ARG
+    bad = rcd.make_config(1000, 64, 64, 48, 8, 49, 64)  # k > E
+    assert upd(C.byref(bad), fake, 64, fake, nul, nul, fake, n.value, nul) == abi.MOE_ERR_INVALID_ARG
+    bad = rcd.make_config(1000, 64, 64, 2048, 8, 4, 64)
+    assert upd(C.byref(bad), fake, 64, fake, nul, nul, fake, n.value, nul) == abi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_router_bias_stage_count() == 4 == len(abi.BIAS_STAGES)
+    prof = lib.moe_router_bias_update_profiled
+    cfg_ok = rcd.make_config(1000, 64, 64, 48, 8, 4, 64)
+    lib.moe_router_bias_ws_bytes(C.byref(cfg_ok), 64, C.byref(n))
+    assert prof(C.byref(cfg_ok), fake, 64, fake, nul, nul, fake, n.value, nul, nul, 5) == abi.MOE_ERR_INVALID_ARG
+    ev = (C.c_void_p * 4)()
+    assert prof(C.byref(cfg_ok), fake, 64, fake, nul, nul, fake, n.value, nul, ev, 4) == abi.MOE_ERR_INVALID_ARG

@@ -133,6 +133,16 @@ def test_shift_equivariance_is_exact():
     assert np.allclose(bias, -(c64 - c64.mean()), rtol=0, atol=1e-6)
 
 
+def test_narrow_range_with_an_infinite_scale():
+    # a range of one fp32 denormal step: n_bins / width overflows fp32; the
+    # minimum stays in bin 0 and the maximum goes to the last bin
+    tiny = np.float32(1e-40)
+    l = np.stack([_col(0, tiny, 0, tiny, tiny), _col(1, 2, 3, 4, 5)], axis=1)
+    hist, lo, hi = rb.histograms(l, 64)
+    assert rb.bin_scale(lo, hi, 64)[0] == np.inf
+    assert hist[0, 0] == 2 and hist[0, 63] == 3 and hist[0].sum() == 5
+
+
 def test_adding_a_constant_to_every_logit_leaves_the_bias():
     rng = np.random.default_rng(6)
     l = rng.integers(-40, 41, size=(400, 9)).astype(np.float32)
