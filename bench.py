@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0
 
 # rocprofv3 kernel names of the stages (substrings that all must match)
 STAGE_KERNEL = {
-    "latent": ("dense_bf16_kernel",),
+    "latent": ("dense1_bf16_kernel",),
     "expert_gate_up": ("ragged_gemm_kernel", ", 1>"),
     "expert_down": ("ragged_gemm_kernel", ", 0>"),
     "shared_gate_up": ("swiglu_bf16_kernel",),

@@ -33,6 +33,8 @@ using core::RowSrc;
 using core::uniform_ptr;
 
 using DenseTile = core::Tile<256, 256, 4, 2, 64, 2>;
+// a third B stage, all 160 KB of LDS: the shared SwiGLU GEMM and single-segment dense GEMMs
+using DenseTile3B = core::Tile<256, 256, 4, 2, 64, 2, 3>;
 using ExpertTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;
 
 constexpr int kGroupM = 8;  // M panels per group of the dense tile order
@@ -150,6 +152,46 @@ __global__ __launch_bounds__(DenseTile::THREADS) void dense_bf16_kernel(GemmDens
     }
     mainloop<TL, false>(a_src, b_src, sg.K / TL::BK, lds, acc);
   }
+  constexpr int ld = TL::BN * 2 + kStagePad;
+  stage_bf16<TL>(acc, lds, ld);
+  __syncthreads();
+  constexpr int cpr = TL::BN * 2 / 16;
+  char* C = static_cast<char*>(g.C);
+  copy_rows<TL>(lds, ld, cpr, min(TL::BM, g.M - m0), min(cpr, (g.N - n0) * 2 / 16),
+                [&](int r) { return C + ((int64_t)(m0 + r) * g.ldc + n0) * 2; });
+}
+
+// One K range (the latent projection): the mid-tile barrier schedule with a
+// third B stage.  A few registers spill around the K loop, none inside it.
+__global__ __launch_bounds__(DenseTile3B::THREADS) void dense1_bf16_kernel(GemmDense g, int tiles_m, int tiles_n) {
+  using TL = DenseTile3B;
+  __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
+  const int t = xcd_order(blockIdx.x, gridDim.x);
+  if (t >= tiles_m * tiles_n) return;
+  int mt, nt;
+  dense_tile(t, tiles_m, tiles_n, mt, nt);
+  const int m0 = mt * TL::BM, n0 = nt * TL::BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const GemmSeg& sg = g.seg[0];
+  RowSrc<TL::A_INS> a_src;
+  RowSrc<TL::B_INS> b_src;
+  const char* A = uniform_ptr(static_cast<const char*>(sg.A));
+  const char* B = uniform_ptr(static_cast<const char*>(sg.B));
+#pragma unroll
+  for (int i = 0; i < TL::A_INS; ++i) {
+    const int m = min(m0 + load_row<TL>(i, wave, lane), g.M - 1);
+    a_src.base[i] = A;
+    a_src.off[i] = (uint32_t)(m * sg.lda * 2) + load_col<TL>(lane);
+  }
+#pragma unroll
+  for (int i = 0; i < TL::B_INS; ++i) {
+    const int n = min(n0 + load_row<TL>(i, wave, lane), g.N - 1);
+    b_src.base[i] = B;
+    b_src.off[i] = (uint32_t)(n * sg.ldb * 2) + load_col<TL>(lane);
+  }
+  Acc<TL> acc;
+  acc.zero();
+  mainloop<TL>(a_src, b_src, sg.K / TL::BK, lds, acc);
   constexpr int ld = TL::BN * 2 + kStagePad;
   stage_bf16<TL>(acc, lds, ld);
   __syncthreads();
@@ -393,13 +435,16 @@ hipError_t launch_ragged_swiglu_bwd_bf16(const RaggedGemm& g, int64_t max_entrie
 hipError_t launch_gemm_dense_bf16(const GemmDense& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int tm = cdiv(g.M, DenseTile::BM), tn = cdiv(g.N, DenseTile::BN);
-  dense_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile::THREADS, 0, s>>>(g, tm, tn);
+  if (g.nseg == 1)
+    dense1_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile3B::THREADS, 0, s>>>(g, tm, tn);
+  else
+    dense_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile::THREADS, 0, s>>>(g, tm, tn);
   return hipGetLastError();
 }
 
 hipError_t launch_swiglu_dense_bf16(const void* A, int64_t lda, const void* Wg, const void* Wu, int G, int F,
                                     int K, int M, void* C, int64_t ldc, hipStream_t s) {
-  using TL = DenseTile;
+  using TL = DenseTile3B;
   if (M <= 0 || G <= 0) return hipSuccess;
   SwigluBf16 p{};
   p.A = static_cast<const char*>(A);
