@@ -1,13 +1,15 @@
 // Pooled-wave dispatch: slot assignment, row scatter into the per-destination
 // pool blocks, and receiver-side binning from the packed id column.
 //
-// Slot assignment is a deterministic stable counting pass per wave: one
-// workgroup of 16 wavefronts per wave, each wavefront owning a contiguous
-// range of the wave's (token, j) assignments.  Pass 1 builds per-wavefront
-// histograms over experts and pools from wavefront match masks (ballots on
-// the key bits), the workgroup scans them across wavefronts, and pass 2
-// walks the ranges again to turn match-mask ranks plus the scanned bases
-// into pool and receiver slots.  No atomics touch the result.
+// Slot assignment is a deterministic stable counting scan per wave over
+// chunks of 1024 (token, j) assignments, one workgroup per (chunk, wave):
+// pass 1 counts each chunk's assignments per expert and per pool; pass 2
+// takes a key's base from the counts of the wave's earlier chunks and ranks
+// the chunk's own assignments with wavefront match masks (ballots on the key
+// bits) and a scan across its wavefronts.  Integer counts make every slot
+// independent of the order in which atomics land.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -16,6 +18,7 @@ namespace {
 
 constexpr int kAssignWaves = 16;
 constexpr int kAssignThreads = kAssignWaves * 64;
+constexpr int kChunk = kAssignThreads;  // assignments per block of the slot scan
 
 __device__ __forceinline__ int key_bits(int n) {  // bits to hold 0..n-1
   int b = 0;
@@ -23,110 +26,127 @@ __device__ __forceinline__ int key_bits(int n) {  // bits to hold 0..n-1
   return b;
 }
 
-__global__ __launch_bounds__(kAssignThreads) void assign_kernel(DispatchArgs a) {
-  extern __shared__ int32_t sh[];
-  const int E = a.E, P = a.P, k = a.k;
-  int32_t* hist_e = sh;                              // [16][E]
-  int32_t* hist_p = hist_e + kAssignWaves * E;       // [16][P]
-  int32_t* demand_p = hist_p + kAssignWaves * P;     // [P]
-  __shared__ int64_t red[kAssignWaves][2];
+// Chunk c of wave w: assignments [c * kChunk, (c + 1) * kChunk) of the wave's
+// (token, j) order.
+struct ChunkRange {
+  int w, c, n, lo, hi;
+  int64_t base;  // flat index of the wave's first assignment
+};
 
-  const int w = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, v = tid >> 6;
-  const int64_t t0 = (int64_t)w * a.Tw;
+__device__ __forceinline__ ChunkRange chunk_range(const DispatchArgs& a) {
+  ChunkRange r;
+  r.w = blockIdx.y;
+  r.c = blockIdx.x;
+  const int64_t t0 = (int64_t)r.w * a.Tw;
   const int64_t t1 = min(a.T, t0 + a.Tw);
-  const int n = t1 > t0 ? (int)((t1 - t0) * k) : 0;
-  const int64_t base = t0 * k;
+  r.n = t1 > t0 ? (int)((t1 - t0) * a.k) : 0;
+  r.base = t0 * a.k;
+  r.lo = min(r.n, r.c * kChunk);
+  r.hi = min(r.n, r.lo + kChunk);
+  return r;
+}
+
+// Pass 1: per chunk, the number of assignments to each expert and to each
+// pool (integer LDS atomics, so the counts do not depend on their order).
+// Also clears the per-wave counters and marks every id slot empty; pass 2
+// then writes the occupied ones.
+__global__ __launch_bounds__(kAssignThreads) void assign_count_kernel(DispatchArgs a) {
+  extern __shared__ int32_t hist[];  // [E + P]
+  const ChunkRange r = chunk_range(a);
+  const int E = a.E, P = a.P, epp = E / P, cap_send = (int)a.cap_send;
+  const int tid = threadIdx.x;
+  if (r.c == 0 && r.w == 0)
+    for (int j = tid; j < 3 * a.W; j += kAssignThreads) a.wave_counts[j] = 0;
+  {
+    // id column of every pool block of this wave: -1 = empty
+    const int64_t nslots = (int64_t)P * cap_send;
+    for (int64_t q = (int64_t)r.c * kAssignThreads + tid; q < nslots; q += (int64_t)gridDim.x * kAssignThreads) {
+      const int pp = (int)(q / cap_send);
+      const int ss = (int)(q - (int64_t)pp * cap_send);
+      reinterpret_cast<int32_t*>(a.pools + ((int64_t)r.w * P + pp) * a.block_bytes + a.ids_offset)[ss] = -1;
+    }
+  }
+  if (r.lo >= r.hi) return;
+  for (int j = tid; j < E + P; j += kAssignThreads) hist[j] = 0;
+  __syncthreads();
+  const int i = r.lo + tid;
+  if (i < r.hi) {
+    const int e = a.topk[r.base + i];
+    if (e >= 0 && e < E) {
+      atomicAdd(&hist[e], 1);
+      atomicAdd(&hist[E + e / epp], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = a.chunk_counts + ((int64_t)r.w * a.n_chunks + r.c) * (E + P);
+  for (int j = tid; j < E + P; j += kAssignThreads) out[j] = hist[j];
+}
+
+// Pass 2: per chunk, the expert and pool ranks of its assignments.  A key's
+// base is its count over the wave's earlier chunks; inside the chunk each
+// wavefront's share comes from match masks (ballots on the key bits) and an
+// exclusive scan across the chunk's wavefronts.  The wave's last chunk also
+// writes the pool occupancy.  Kept / sender-dropped / receiver-dropped
+// counts are integer atomics into the per-wave counters.
+__global__ __launch_bounds__(kAssignThreads) void assign_slots_kernel(DispatchArgs a) {
+  extern __shared__ int32_t sh[];
+  const int E = a.E, P = a.P, K = E + P;
+  int32_t* wh = sh;                          // [16][E + P]: per-wavefront counts, then their bases
+  __shared__ int64_t red[kAssignWaves][3];
+  const ChunkRange r = chunk_range(a);
+  const int tid = threadIdx.x, lane = tid & 63, v = tid >> 6;
   const int epp = E / P;
   const int ebits = key_bits(E), pbits = key_bits(P);
   const int cap_send = (int)a.cap_send, cap_recv = (int)a.cap_recv;
-
-  for (int i = tid; i < kAssignWaves * (E + P); i += kAssignThreads) sh[i] = 0;
+  if (r.n == 0) {  // an empty wave: nothing sent
+    if (r.c == 0)
+      for (int pp = tid; pp < P; pp += kAssignThreads) a.pool_count[r.w * P + pp] = 0;
+    return;
+  }
+  if (r.lo >= r.hi) return;
+  const bool last = r.hi == r.n;
+  for (int j = tid; j < kAssignWaves * K; j += kAssignThreads) wh[j] = 0;
   __syncthreads();
 
-  // contiguous range of this wavefront, a multiple of 64 assignments
-  const int per = ((n + kAssignWaves * 64 - 1) / (kAssignWaves * 64)) * 64;
-  const int lo = min(n, v * per), hi = min(n, lo + per);
+  const int i = r.lo + v * 64 + lane;
+  const int e_in = i < r.hi ? a.topk[r.base + i] : 0;
+  const bool valid = i < r.hi && e_in >= 0 && e_in < E;
+  const int e = valid ? e_in : 0;
+  const int p = e / epp;
   const uint64_t lt = lanemask_lt();
+  const uint64_t act = ballot64(valid);
+  const uint64_t me = match_key((uint32_t)e, ebits, act);
+  const uint64_t mp = match_key((uint32_t)p, pbits, act);
+  if (valid && (me & lt) == 0) wh[v * K + e] = __popcll(me);
+  if (valid && (mp & lt) == 0) wh[v * K + E + p] = __popcll(mp);
+  __syncthreads();
 
-  // pass 1: per-wavefront histograms (expert ids outside [0, E) take no
-  // slot and count as sender drops)
-  for (int it = lo; it < hi; it += 64) {
-    const int i = it + lane;
-    const int e_in = i < hi ? a.topk[base + i] : 0;
-    const bool valid = i < hi && e_in >= 0 && e_in < E;
-    const int e = valid ? e_in : 0;
-    const int p = e / epp;
-    const uint64_t act = ballot64(valid);
-    const uint64_t me = match_key((uint32_t)e, ebits, act);
-    const uint64_t mp = match_key((uint32_t)p, pbits, act);
-    if (valid && (me & lt) == 0) hist_e[v * E + e] += __popcll(me);
-    if (valid && (mp & lt) == 0) hist_p[v * P + p] += __popcll(mp);
+  // per key: the count over earlier chunks, then an exclusive scan over
+  // this chunk's wavefronts
+  const int32_t* cnt = a.chunk_counts + (int64_t)r.w * a.n_chunks * K;
+  for (int j = tid; j < K; j += kAssignThreads) {
+    int run = 0;
+    for (int c = 0; c < r.c; ++c) run += cnt[(int64_t)c * K + j];
+    for (int u = 0; u < kAssignWaves; ++u) {
+      const int x = wh[u * K + j];
+      wh[u * K + j] = run;
+      run += x;
+    }
+    if (last && j >= E) a.pool_count[r.w * P + (j - E)] = min(run, cap_send);
   }
   __syncthreads();
 
-  // exclusive scan across wavefronts; totals are the wave's demand
-  for (int e = tid; e < E; e += kAssignThreads) {
-    int run = 0;
-    for (int u = 0; u < kAssignWaves; ++u) {
-      const int c = hist_e[u * E + e];
-      hist_e[u * E + e] = run;
-      run += c;
-    }
-  }
-  int64_t sd = 0;
-  for (int p = tid; p < P; p += kAssignThreads) {
-    int run = 0;
-    for (int u = 0; u < kAssignWaves; ++u) {
-      const int c = hist_p[u * P + p];
-      hist_p[u * P + p] = run;
-      run += c;
-    }
-    demand_p[p] = run;
-    a.pool_count[w * P + p] = min(run, cap_send);
-    sd += max(0, run - cap_send);
-  }
-  __syncthreads();
-
-  // empty slots of the id column
-  for (int64_t q = tid; q < (int64_t)P * cap_send; q += kAssignThreads) {
-    const int p = (int)(q / cap_send);
-    const int s = (int)(q - (int64_t)p * cap_send);
-    if (s >= demand_p[p]) {
-      int32_t* ids = reinterpret_cast<int32_t*>(a.pools + ((int64_t)w * P + p) * a.block_bytes + a.ids_offset);
-      ids[s] = -1;
-    }
-  }
-
-  // pass 2: slots
-  int64_t kept = 0, rd = 0;
-  for (int it = lo; it < hi; it += 64) {
-    const int i = it + lane;
-    const int e_in = i < hi ? a.topk[base + i] : 0;
-    const bool valid = i < hi && e_in >= 0 && e_in < E;
-    const int e = valid ? e_in : 0;
-    const int p = e / epp;
-    if (i < hi && !valid) {
-      a.pool_slot[base + i] = -1;
-      a.recv_slot[base + i] = -1;
+  int64_t kept = 0, sd = 0, rd = 0;
+  if (i < r.hi) {
+    int ps = -1, rs = -1;
+    if (!valid) {
       ++sd;
-    }
-    const uint64_t act = ballot64(valid);
-    const uint64_t me = match_key((uint32_t)e, ebits, act);
-    const uint64_t mp = match_key((uint32_t)p, pbits, act);
-    int rank_e = 0, rank_p = 0;
-    if (valid) {
-      rank_e = hist_e[v * E + e] + __popcll(me & lt);
-      rank_p = hist_p[v * P + p] + __popcll(mp & lt);
-    }
-    if (valid && (me & lt) == 0) hist_e[v * E + e] = rank_e + __popcll(me);
-    if (valid && (mp & lt) == 0) hist_p[v * P + p] = rank_p + __popcll(mp);
-    if (valid) {
-      int ps = -1, rs = -1;
+    } else {
+      const int rank_p = wh[v * K + E + p] + __popcll(mp & lt);
+      const int rank_e = wh[v * K + e] + __popcll(me & lt);
       if (rank_p < cap_send) {
         ps = rank_p;
-        int32_t* ids = reinterpret_cast<int32_t*>(a.pools + ((int64_t)w * P + p) * a.block_bytes + a.ids_offset);
-        ids[ps] = e;
+        reinterpret_cast<int32_t*>(a.pools + ((int64_t)r.w * P + p) * a.block_bytes + a.ids_offset)[ps] = e;
         // every earlier assignment to e shares pool p and was sent, so the
         // expert rank is the receiver's binning order
         if (rank_e < cap_recv) {
@@ -135,35 +155,24 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(DispatchArgs a) 
         } else {
           ++rd;
         }
+      } else {
+        ++sd;
       }
-      a.pool_slot[base + i] = ps;
-      a.recv_slot[base + i] = rs;
     }
+    a.pool_slot[r.base + i] = ps;
+    a.recv_slot[r.base + i] = rs;
   }
-  // workgroup reduction of the wave's counters
   for (int m = 32; m >= 1; m >>= 1) {
     kept += __shfl_xor(kept, m);
+    sd += __shfl_xor(sd, m);
     rd += __shfl_xor(rd, m);
   }
-  // sender drops were summed per pool by the threads that scanned them
-  __shared__ int64_t red_sd[kAssignWaves];
-  for (int m = 32; m >= 1; m >>= 1) sd += __shfl_xor(sd, m);
-  if (lane == 0) {
-    red[v][0] = kept;
-    red[v][1] = rd;
-    red_sd[v] = sd;
-  }
+  if (lane == 0) red[v][0] = kept, red[v][1] = sd, red[v][2] = rd;
   __syncthreads();
-  if (tid == 0) {
-    int64_t K = 0, R = 0, S = 0;
-    for (int u = 0; u < kAssignWaves; ++u) {
-      K += red[u][0];
-      R += red[u][1];
-      S += red_sd[u];
-    }
-    a.wave_counts[w * 3 + 0] = K;
-    a.wave_counts[w * 3 + 1] = S;
-    a.wave_counts[w * 3 + 2] = R;
+  if (tid < 3) {
+    int64_t t = 0;
+    for (int u = 0; u < kAssignWaves; ++u) t += red[u][tid];
+    if (t) atomicAdd(reinterpret_cast<unsigned long long*>(a.wave_counts + r.w * 3 + tid), (unsigned long long)t);
   }
 }
 
@@ -291,15 +300,22 @@ __global__ void zero_i64_kernel(int64_t* p, int n) {
 
 }  // namespace
 
+int assign_chunks(int64_t Tw, int k) { return (int)std::max<int64_t>(1, (Tw * k + kChunk - 1) / kChunk); }
+
 hipError_t launch_assign(const DispatchArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(int32_t) * ((size_t)kAssignWaves * (a.E + a.P) + a.P);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(assign_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const dim3 grid((unsigned)a.n_chunks, (unsigned)a.W);
+  const size_t lds1 = sizeof(int32_t) * (size_t)(a.E + a.P);
+  assign_count_kernel<<<grid, kAssignThreads, lds1, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds2 = sizeof(int32_t) * (size_t)kAssignWaves * (a.E + a.P);
+  if (lds2 > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(assign_slots_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
     if (e != hipSuccess) return e;
   }
-  assign_kernel<<<a.W, kAssignThreads, lds, s>>>(a);
-  hipError_t e = hipGetLastError();
+  assign_slots_kernel<<<grid, kAssignThreads, lds2, s>>>(a);
+  e = hipGetLastError();
   if (e != hipSuccess || !a.counts) return e;
   finalize_counts_kernel<<<1, 64, 0, s>>>(a.wave_counts, a.W, a.counts);
   return hipGetLastError();

@@ -95,7 +95,11 @@ struct DispatchArgs {
   int64_t block_bytes, ids_offset, row_bytes;
   int64_t* wave_counts;  // [W][3] workspace
   int64_t* counts;       // [3] or null
+  int32_t* chunk_counts; // [W][n_chunks][E + P] workspace: per-chunk key counts
+  int n_chunks;          // chunks of the slot scan per wave (assign_chunks)
 };
+// Chunks of the slot scan per wave: ceil(Tw * k / 1024), at least 1.
+int assign_chunks(int64_t Tw, int k);
 hipError_t launch_assign(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_scatter_rows(const DispatchArgs& a, const void* z, hipStream_t s);
 hipError_t launch_recv_bin(const DispatchArgs& a, int32_t* bank_rows,

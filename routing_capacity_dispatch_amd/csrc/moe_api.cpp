@@ -151,6 +151,7 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
 
   Carver d{nullptr, 0};
   d.take(W * 3 * 8);  // per-wave counters
+  d.take(W * moe::assign_chunks(Tw, k) * (int64_t)(E + P) * 4);  // per-chunk key counts of the slot scan
   p->dispatch_ws_bytes = d.used;
 
   Carver x{nullptr, 0};
@@ -312,8 +313,11 @@ moe_status run_dispatch(const moe_config* c, const moe_plan& p, const int32_t* t
                         hipStream_t s, Marks* m) {
   Carver cv{static_cast<char*>(ws), 0};
   int64_t* wave_counts = static_cast<int64_t*>(cv.take(c->n_waves * 3 * 8));
-  const moe::DispatchArgs a =
+  moe::DispatchArgs a =
       dispatch_args(c, p, topk, pools, pool_slot, recv_slot, pool_count, wave_counts, counts);
+  a.n_chunks = moe::assign_chunks(p.tokens_per_wave, c->top_k);
+  a.chunk_counts = static_cast<int32_t*>(
+      cv.take(c->n_waves * (int64_t)a.n_chunks * (c->n_experts + c->n_pools) * 4));
   hipError_t e = moe::launch_assign(a, s);
   if (e == hipSuccess && m) e = m->mark(s);
   if (e == hipSuccess) e = moe::launch_scatter_rows(a, z, s);
