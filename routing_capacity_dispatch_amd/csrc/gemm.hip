@@ -332,6 +332,7 @@ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 hipError_t launch_gemm_dense(int in_dt, int out_dt, const GemmDense& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (in_dt == DT_BF16 && out_dt == DT_BF16) return launch_gemm_dense_bf16(g, s);
+  if (in_dt == DT_BF16 && out_dt == DT_F32 && dense_f32out_supported(g)) return launch_dense_f32out_bf16(g, s);
   const dim3 grid(cdiv(g.N, BN), cdiv(g.M, BM));
   if (in_dt == DT_BF16 && out_dt == DT_F32)
     gemm_dense_kernel<bf16_t, float><<<grid, NTHR, 0, s>>>(g);

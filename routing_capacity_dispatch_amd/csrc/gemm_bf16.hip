@@ -36,6 +36,9 @@ using DenseTile = core::Tile<256, 256, 4, 2, 64, 2>;
 // a third B stage, all 160 KB of LDS: the shared SwiGLU GEMM and single-segment dense GEMMs
 using DenseTile3B = core::Tile<256, 256, 4, 2, 64, 2, 3>;
 using ExpertTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;
+// fp32 output (the router logits): 4 wavefronts of 64 x 48; E = 384 columns
+// are four N tiles, so the Marin-shaped router GEMM is 512 tiles, two per CU
+using RouterTile = core::Tile<128, 96, 2, 2, 64, 2>;
 
 constexpr int kGroupM = 8;  // M panels per group of the dense tile order
 constexpr int kStagePad = 16;
@@ -199,6 +202,55 @@ __global__ __launch_bounds__(DenseTile3B::THREADS) void dense1_bf16_kernel(GemmD
   char* C = static_cast<char*>(g.C);
   copy_rows<TL>(lds, ld, cpr, min(TL::BM, g.M - m0), min(cpr, (g.N - n0) * 2 / 16),
                 [&](int r) { return C + ((int64_t)(m0 + r) * g.ldc + n0) * 2; });
+}
+
+// bf16 operands, fp32 output, one K range (the router logits).
+__global__ __launch_bounds__(RouterTile::THREADS) void dense_f32out_kernel(GemmDense g, int tiles_m, int tiles_n) {
+  using TL = RouterTile;
+  constexpr int ld = TL::BN * 4 + kStagePad;
+  constexpr int kLds = TL::MAIN_LDS > TL::BM * ld ? TL::MAIN_LDS : TL::BM * ld;
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
+  const int t = xcd_order(blockIdx.x, gridDim.x);
+  if (t >= tiles_m * tiles_n) return;
+  int mt, nt;
+  dense_tile(t, tiles_m, tiles_n, mt, nt);
+  const int m0 = mt * TL::BM, n0 = nt * TL::BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const GemmSeg& sg = g.seg[0];
+  RowSrc<TL::A_INS> a_src;
+  RowSrc<TL::B_INS> b_src;
+  const char* A = uniform_ptr(static_cast<const char*>(sg.A));
+  const char* B = uniform_ptr(static_cast<const char*>(sg.B));
+#pragma unroll
+  for (int i = 0; i < TL::A_INS; ++i) {
+    const int m = min(m0 + load_row<TL>(i, wave, lane), g.M - 1);
+    a_src.base[i] = A;
+    a_src.off[i] = (uint32_t)(m * sg.lda * 2) + load_col<TL>(lane);
+  }
+#pragma unroll
+  for (int i = 0; i < TL::B_INS; ++i) {
+    const int n = min(n0 + load_row<TL>(i, wave, lane), g.N - 1);
+    b_src.base[i] = B;
+    b_src.off[i] = (uint32_t)(n * sg.ldb * 2) + load_col<TL>(lane);
+  }
+  Acc<TL> acc;
+  acc.zero();
+  mainloop<TL>(a_src, b_src, sg.K / TL::BK, lds, acc);
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+#pragma unroll
+  for (int mi = 0; mi < TL::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < TL::NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = acc_row<TL>(wm, mi, lane, r), col = acc_col<TL>(wn, ni, lane);
+        *reinterpret_cast<float*>(lds + row * ld + col * 4) = acc.v[mi][ni][r];
+      }
+  __syncthreads();
+  constexpr int cpr = TL::BN * 4 / 16;
+  char* C = static_cast<char*>(g.C);
+  copy_rows<TL>(lds, ld, cpr, min(TL::BM, g.M - m0), min(cpr, (g.N - n0) * 4 / 16),
+                [&](int r) { return C + ((int64_t)(m0 + r) * g.ldc + n0) * 4; });
 }
 
 // ------------------------------------------------------------------ SwiGLU
@@ -439,6 +491,20 @@ hipError_t launch_gemm_dense_bf16(const GemmDense& g, hipStream_t s) {
     dense1_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile3B::THREADS, 0, s>>>(g, tm, tn);
   else
     dense_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile::THREADS, 0, s>>>(g, tm, tn);
+  return hipGetLastError();
+}
+
+bool dense_f32out_supported(const GemmDense& g) {
+  // whole 16-byte chunks of fp32 output rows, one K range of whole K tiles,
+  // 16-byte aligned operand rows
+  return g.nseg == 1 && g.N % 4 == 0 && g.seg[0].K % RouterTile::BK == 0 && g.seg[0].lda % 8 == 0 &&
+         g.seg[0].ldb % 8 == 0 && g.ldc % 4 == 0;
+}
+
+hipError_t launch_dense_f32out_bf16(const GemmDense& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const int tm = cdiv(g.M, RouterTile::BM), tn = cdiv(g.N, RouterTile::BN);
+  dense_f32out_kernel<<<pad8((int64_t)tm * tn), RouterTile::THREADS, 0, s>>>(g, tm, tn);
   return hipGetLastError();
 }
 

@@ -68,6 +68,10 @@ hipError_t launch_expert_down(int dt, const ExpertDown& a, hipStream_t s);
 // bf16 paths on the gfx950 GEMM core (gemm_bf16.hip); the generic dense
 // launchers above dispatch to them for bf16 inputs and outputs.
 hipError_t launch_gemm_dense_bf16(const GemmDense& g, hipStream_t s);
+// bf16 operands, fp32 output on the gfx950 core (the router logits), for
+// one K range of whole K tiles and whole 16-byte output chunks.
+bool dense_f32out_supported(const GemmDense& g);
+hipError_t launch_dense_f32out_bf16(const GemmDense& g, hipStream_t s);
 hipError_t launch_swiglu_dense_bf16(const void* A, int64_t lda, const void* Wg, const void* Wu, int G,
                                     int F, int K, int M, void* C, int64_t ldc, hipStream_t s);
 
