@@ -85,23 +85,38 @@ __global__ __launch_bounds__(64) void bwd_gidx_ragged_kernel(const int32_t* __re
 
 // dst row i = the pool row gidx[i] (block = i / block_rows at block_bytes
 // apart, rows row_bytes apart inside a block), or zeros where gidx[i] < 0.
-// 16-byte chunks, grid-stride.
+// One wavefront per row (grid-stride over rows), six 16-byte chunks per
+// lane in flight.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src, int block_rows,
                                                           int64_t block_bytes, int64_t row_bytes,
                                                           const int32_t* __restrict__ gidx,
                                                           const int32_t* __restrict__ nrows, char* __restrict__ dst) {
+  constexpr int CPL = 6;
+  const int lane = threadIdx.x & 63;
   const int cpr = (int)(row_bytes / 16);
-  const int64_t total = (int64_t)(*nrows) * cpr;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
-    const int64_t i = q / cpr;
-    const int c = (int)(q - i * cpr);
+  const int64_t n = *nrows;
+  for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < n; i += (int64_t)gridDim.x * 4) {
     const int fi = gidx[i];
-    uint4 v = make_uint4(0, 0, 0, 0);
+    const char* srow = nullptr;
     if (fi >= 0) {
       const int blk = fi / block_rows;
-      v = ld16(src + blk * block_bytes + (int64_t)(fi - blk * block_rows) * row_bytes + (int64_t)c * 16);
+      srow = src + blk * block_bytes + (int64_t)(fi - blk * block_rows) * row_bytes;
     }
-    st16(dst + i * row_bytes + (int64_t)c * 16, v);
+    char* drow = dst + i * row_bytes;
+    for (int c0 = 0; c0 < cpr; c0 += 64 * CPL) {
+      uint4 v[CPL];
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = c0 + u * 64 + lane;
+        v[u] = make_uint4(0, 0, 0, 0);
+        if (srow && c < cpr) v[u] = ld16(srow + (int64_t)c * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < cpr) st16(drow + (int64_t)c * 16, v[u]);
+      }
+    }
   }
 }
 
@@ -221,9 +236,8 @@ hipError_t launch_gather_rows(const void* src, int block_rows, int64_t block_byt
                               const int32_t* gidx, const int32_t* nrows, int64_t max_rows, void* dst,
                               hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  const int64_t chunks = max_rows * (row_bytes / 16);
-  const int64_t want = (chunks + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  const int64_t want = (max_rows + 3) / 4;  // four rows per block
+  const unsigned blocks = (unsigned)(want < 16384 ? want : 16384);
   gather_rows_kernel<<<blocks, 256, 0, s>>>(static_cast<const char*>(src), block_rows, block_bytes, row_bytes,
                                             gidx, nrows, static_cast<char*>(dst));
   return hipGetLastError();

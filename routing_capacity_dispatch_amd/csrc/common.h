@@ -120,27 +120,28 @@ template <typename T>
 __device__ __forceinline__ void combine_rows(const char* __restrict__ base, int64_t row, float g, int k,
                                              int64_t row_bytes, char* __restrict__ dst) {
   constexpr int EPC = Chunk<T>::kElems;
+  constexpr int CPL = 6;  // 16-byte chunks per lane per pass: a 3072-wide bf16 row in one pass
   const int lane = threadIdx.x & 63;
   const int chunks = (int)(row_bytes / 16);
-  for (int seg = 0; seg < chunks; seg += 64 * 8) {
-    float acc[8][EPC];
+  for (int seg = 0; seg < chunks; seg += 64 * CPL) {
+    float acc[CPL][EPC];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < CPL; ++i)
 #pragma unroll
       for (int q = 0; q < EPC; ++q) acc[i][q] = 0.0f;
     for (int j = 0; j < k; j += 2) {
       const int64_t r0 = shfl64(row, j);
       const int64_t r1 = j + 1 < k ? shfl64(row, j + 1) : -1;
       const float g0 = __shfl(g, j), g1 = __shfl(g, j + 1);
-      uint4 v0[8], v1[8];
+      uint4 v0[CPL], v1[CPL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < CPL; ++i) {
         const int c = seg + i * 64 + lane;
         if (c < chunks && r0 >= 0) v0[i] = ld16(base + r0 * row_bytes + (int64_t)c * 16);
         if (c < chunks && r1 >= 0) v1[i] = ld16(base + r1 * row_bytes + (int64_t)c * 16);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < CPL; ++i) {
         const int c = seg + i * 64 + lane;
         if (c >= chunks) continue;
         float f[EPC];
@@ -157,7 +158,7 @@ __device__ __forceinline__ void combine_rows(const char* __restrict__ base, int6
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < CPL; ++i) {
       const int c = seg + i * 64 + lane;
       if (c < chunks) st16(dst + (int64_t)c * 16, pack(acc[i], T{}));
     }
