@@ -76,6 +76,11 @@ DISPATCH_CASES = [
     ("many_experts", 2048, 1024, 1024, 16, 2, 64, "bf16", 0.002, (11, 10), (23, 20), (0, 0)),
     ("many_pools", 3000, 256, 128, 6, 5, 128, "bf16", 0.01, (11, 10), (23, 20), (0, 0)),
     ("wide_rows", 300, 16, 4, 2, 3, 8192, "f32", 0.1, (11, 10), (23, 20), (0, 0)),
+    # the slot scan works in chunks of 1024 assignments per wave: a wave of
+    # exactly one chunk, and waves one token past it (a chunk of 8)
+    ("chunk_exact", 384, 64, 16, 8, 3, 64, "bf16", 0.3, (11, 10), (23, 20), (0, 0)),
+    ("chunk_plus_one", 387, 64, 16, 8, 3, 64, "bf16", 0.3, (11, 10), (23, 20), (0, 0)),
+    ("chunk_mixed", 386, 64, 16, 8, 3, 64, "bf16", 0.3, (11, 10), (23, 20), (0, 0)),  # waves 129, 129, 128
 ]
 
 
