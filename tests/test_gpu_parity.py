@@ -126,6 +126,48 @@ def test_dispatch(case):
                            want.view(torch.int16) if dt == "bf16" else want.view(torch.int32))
 
 
+def _random_dispatch_cases(n=24, seed=20260):
+    """Seeded random shapes for the slot scan: T, E (with P dividing it), k,
+    W, the skew of the expert draw and the capacity factors or explicit
+    capacities, so that sender and receiver drops fall at random places
+    across chunk and wave boundaries."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([4, 12, 16, 48, 64, 96, 384, 1024]))
+        divisors = [d for d in range(1, E + 1) if E % d == 0]
+        P = int(rng.choice(divisors))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        W = int(rng.integers(1, 6))
+        T = int(rng.integers(1, 6000))
+        skew = float(rng.choice([0.0, 0.01, 0.05, 0.3]))
+        sc = (int(rng.integers(0, 16)), 10)
+        rc = (int(rng.integers(0, 16)), 10)
+        rows = (0, 0) if rng.random() < 0.7 else (int(rng.integers(1, 200)), int(rng.integers(1, 200)))
+        cases.append((f"random{i}", T, E, P, k, W, 64, "bf16", skew, sc, rc, rows))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_dispatch_cases(), ids=lambda c: c[0])
+def test_dispatch_random(case):
+    d = dev()
+    say("dispatch", case)
+    cfg, topk, z, out = _dispatch_case(case, d)
+    torch.cuda.synchronize()
+    name, T, E, P, k, W = case[:6]
+    p = out["plan"]
+    ref = oracle.assign_slots(topk.numpy(), E, P, W, p["cap_send"], p["cap_recv"])
+    assert np.array_equal(np_i(out["pool_slot"]), ref["pool_slot"])
+    assert np.array_equal(np_i(out["recv_slot"]), ref["recv_slot"])
+    assert np.array_equal(np_i(out["pool_count"]), ref["pool_count"])
+    ec = np_i(out["expert_count"])
+    assert np.array_equal(ec, ref["expert_count"])
+    assert np.array_equal(bank_valid(np_i(out["bank_rows"]), ec), ref["bank_rows"])
+    assert np_i(out["counts"]).tolist() == [ref["kept"], ref["sender_dropped"], ref["receiver_dropped"]]
+    _, ids = rcd.pool_views(cfg, out["pools"])
+    assert np.array_equal(np_i(ids), ref["ids"])
+
+
 def test_dispatch_out_of_range_ids_are_dropped():
     d = dev()
     T, E, P, k = 64, 16, 4, 2
