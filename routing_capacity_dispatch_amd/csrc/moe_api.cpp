@@ -111,6 +111,7 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
       (c->n_shared > 0 && c->d_ff_shared % 64))
     return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 3) return MOE_ERR_UNSUPPORTED;
+  if (c->n_waves > 65535) return MOE_ERR_UNSUPPORTED;  // the slot scan's grid has one row per wave
 
   const int64_t T = c->T, W = c->n_waves, E = c->n_experts, P = c->n_pools, k = c->top_k;
   const int64_t Tw = ceil_div(T, W);

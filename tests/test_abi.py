@@ -120,6 +120,7 @@ def _status(fn):
     ("d_latent", 100, abi.MOE_ERR_UNSUPPORTED),     # not a multiple of 64
     ("d_ff", 96, abi.MOE_ERR_UNSUPPORTED),
     ("n_shared", 4, abi.MOE_ERR_UNSUPPORTED),
+    ("n_waves", 65536, abi.MOE_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(lib, field, value, status):
     cfg = rcd.config_of(synth.workload("tiny_fp32"))
