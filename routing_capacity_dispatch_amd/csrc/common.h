@@ -49,6 +49,14 @@ __device__ __forceinline__ void st16(void* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
 
+// Streaming load for data read once per step (nontemporal hint: the lines
+// are not kept in the caches for reuse)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Unpack a 16-byte chunk of T into floats: 4 (f32) or 8 (bf16) values.
 __device__ __forceinline__ void unpack(const uint4& v, float* out, float) {
   out[0] = __uint_as_float(v.x);
@@ -115,7 +123,8 @@ __device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
 // One wavefront: dst = sum over j < k of g_j * rows[r_j], where lane j holds
 // (r_j, g_j) in (row, g) and r_j < 0 adds nothing; fp32 accumulation in j
 // order, stored as T.  Rows are row_bytes (a multiple of 16) apart from
-// base.  Two rows' loads are in flight per step.
+// base.  Two rows' loads are in flight per step.  Each row is read once, so
+// the reads carry the nontemporal hint.
 template <typename T>
 __device__ __forceinline__ void combine_rows(const char* __restrict__ base, int64_t row, float g, int k,
                                              int64_t row_bytes, char* __restrict__ dst) {
@@ -137,8 +146,8 @@ __device__ __forceinline__ void combine_rows(const char* __restrict__ base, int6
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = seg + i * 64 + lane;
-        if (c < chunks && r0 >= 0) v0[i] = ld16(base + r0 * row_bytes + (int64_t)c * 16);
-        if (c < chunks && r1 >= 0) v1[i] = ld16(base + r1 * row_bytes + (int64_t)c * 16);
+        if (c < chunks && r0 >= 0) v0[i] = ld16_stream(base + r0 * row_bytes + (int64_t)c * 16);
+        if (c < chunks && r1 >= 0) v1[i] = ld16_stream(base + r1 * row_bytes + (int64_t)c * 16);
       }
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {

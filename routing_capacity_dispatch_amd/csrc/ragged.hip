@@ -16,6 +16,7 @@ namespace {
 
 constexpr int kSortWaves = 16;
 constexpr int kSortThreads = kSortWaves * 64;
+constexpr int kTileListBlocks = 32;  // workgroups writing the tile lists
 
 __device__ __forceinline__ int key_bits_of(int n) {
   int b = 0;
@@ -153,59 +154,57 @@ __global__ __launch_bounds__(256) void ragged_scatter_kernel(const char* __restr
   scatter_row(z + t * row_bytes, dst, k, row_bytes);
 }
 
-// Tile lists of the grouped GEMMs (one workgroup, thread e = expert e):
-// expert e owns ceil(count_e / bm) M tiles; list entries are (e, n tile,
-// m tile) in that order with the M tile fastest, so the M tiles that share a
-// weight tile are neighbours.  Two lists, for two N tile counts.
+// Tile lists of the grouped expert GEMMs: expert e gets ceil(rows_e / bm) M
+// tiles; list0 (list1) holds (e, N tile, M tile) for tiles_n0 (tiles_n1) N
+// tiles per M tile, experts in order, then N tiles, then M tiles (M fastest,
+// so the M tiles sharing a weight tile are neighbours).  Every block scans
+// the experts' M-tile counts in LDS, then the grid writes the entries
+// (12 bytes each) with consecutive threads on consecutive entries: entry q of
+// a list with tn N tiles belongs to the expert whose M-tile range holds
+// q / tn.
 __global__ __launch_bounds__(1024) void ragged_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                              int tiles_n0, int tiles_n1,
                                                              int32_t* __restrict__ list0,
                                                              int32_t* __restrict__ list1,
                                                              int32_t* __restrict__ ntiles) {
-  __shared__ int32_t mt[1024];
+  __shared__ int32_t first[1025];  // M tiles before expert e; first[E] = all
   __shared__ int32_t part[16];
+  __shared__ int32_t total;
   const int e = threadIdx.x;
   const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
   const int m = (cnt + bm - 1) / bm;
-  mt[e] = m;
-  const int lane = e & 63, w = e >> 6;
-  int v = m;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
-  if (lane == 63) part[w] = v;
+  const int ex = block_excl_scan_1024(m, part, &total);
+  if (e < E) first[e] = ex;
+  if (e == 0) first[E] = total;
   __syncthreads();
-  if (e == 0) {
-    int s = 0;
-    for (int i = 0; i < 16; ++i) {
-      const int t = part[i];
-      part[i] = s;
-      s += t;
+  const int64_t n0 = (int64_t)total * tiles_n0, n1 = (int64_t)total * tiles_n1;
+  if (blockIdx.x == 0 && e == 0) {
+    ntiles[0] = (int32_t)n0;
+    ntiles[1] = (int32_t)n1;
+  }
+  for (int64_t q = (int64_t)blockIdx.x * 1024 + e; q < n0 + n1; q += (int64_t)gridDim.x * 1024) {
+    const bool one = q >= n0;
+    const int64_t qq = one ? q - n0 : q;
+    const int tn = one ? tiles_n1 : tiles_n0;
+    const int v = (int)(qq / tn);
+    // largest x < E with first[x] <= v: the expert whose M-tile range
+    // [first[x], first[x + 1]) holds v (experts without rows share their
+    // first with the next expert and are skipped)
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= v)
+        lo = mid;
+      else
+        hi = mid - 1;
     }
-  }
-  __syncthreads();
-  const int incl = v + part[w];
-  const int first = incl - m;  // M tiles before expert e
-  if (e < E) {
-    for (int nt = 0; nt < tiles_n0; ++nt)
-      for (int i = 0; i < m; ++i) {
-        int32_t* q = list0 + 3 * ((int64_t)first * tiles_n0 + nt * m + i);
-        q[0] = e;
-        q[1] = nt;
-        q[2] = i;
-      }
-    for (int nt = 0; nt < tiles_n1; ++nt)
-      for (int i = 0; i < m; ++i) {
-        int32_t* q = list1 + 3 * ((int64_t)first * tiles_n1 + nt * m + i);
-        q[0] = e;
-        q[1] = nt;
-        q[2] = i;
-      }
-  }
-  if (e == E - 1) {
-    ntiles[0] = incl * tiles_n0;
-    ntiles[1] = incl * tiles_n1;
+    const int me = first[lo + 1] - first[lo];
+    const int rem = (int)(qq - (int64_t)first[lo] * tn);
+    const int nt = rem / me;
+    int32_t* d = (one ? list1 : list0) + 3 * qq;
+    d[0] = lo;
+    d[1] = nt;
+    d[2] = rem - nt * me;
   }
 }
 
@@ -264,7 +263,7 @@ hipError_t launch_ragged_scatter(const void* z, const int32_t* row_of, int64_t T
 
 hipError_t launch_ragged_tiles(const int32_t* offsets, int E, int bm, int tiles_n0, int tiles_n1,
                                int32_t* list0, int32_t* list1, int32_t* ntiles, hipStream_t s) {
-  ragged_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, bm, tiles_n0, tiles_n1, list0, list1, ntiles);
+  ragged_tiles_kernel<<<kTileListBlocks, 1024, 0, s>>>(offsets, E, bm, tiles_n0, tiles_n1, list0, list1, ntiles);
   return hipGetLastError();
 }
 

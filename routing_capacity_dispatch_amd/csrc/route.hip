@@ -1,41 +1,70 @@
 // Router selection: top-k by fl32(logit + bias) with ties to the lower expert
 // index, and gates = softmax over the selected raw logits.
 //
-// One wavefront per token.  Lane l holds experts l, l+64, ... as 64-bit keys
-// (order-preserving fp32 score bits << 32 | ~expert), so a single unsigned
-// max picks the highest score and, among equal scores, the lowest index.
-// k rounds of a wavefront max select the experts in output order.
+// One wavefront per token.  Lane l holds experts l, l+64, ... as unsigned
+// keys that order the fp32 scores (0 marks an absent or taken expert).  Each
+// of k rounds takes the wavefront's largest key (DPP within rows of 16
+// lanes, then the four row results read into scalar registers) and, among
+// the experts holding it, the lowest index (ballots: the first register
+// slot with a match, then its lowest lane), so the experts come out in
+// output order with ties to the lower index.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+// DPP controls: lane i of each row of 16 reads lane i^1, i^2 (quad
+// permutes), 7-i within its half row, 15-i within its row
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, int ctrl_sel) {
+  uint32_t o;
+  switch (ctrl_sel) {
+    case 0: o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xF, 0xF, false); break;
+    case 1: o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xF, 0xF, false); break;
+    case 2: o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, false); break;
+    default: o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xF, 0xF, false); break;
+  }
+  return o > v ? o : v;
 }
 
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+// Largest value over the wavefront, wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint64_t o = shfl_xor64(v, m);
-    v = o > v ? o : v;
+  for (int c = 0; c < 4; ++c) v = dpp_max(v, c);  // every lane: its row's max
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+// Lane i^1, i^2, 7-i (half row), 15-i (row) of v, as a float.
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
+  const int b = __float_as_int(v);
+  switch (ctrl_sel) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, kDppXor1, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, kDppXor2, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, kDppHalfMirror, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, kDppMirror, 0xF, 0xF, false));
   }
-  return v;
+}
+__device__ __forceinline__ float row_lane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  for (int c = 0; c < 4; ++c) v = fmaxf(v, dpp_f(v, c));
+  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  for (int c = 0; c < 4; ++c) v += dpp_f(v, c);
+  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
 }
 
 // Total order on finite fp32 scores as unsigned keys; -0 is mapped to +0.
@@ -55,23 +84,29 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float* __restrict
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + t * E;
-  uint64_t key[NPER];
+  uint32_t key[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = i * 64 + lane;
     key[i] = 0;
-    if (e < E) {
-      const float s = row[e] + (bias ? bias[e] : 0.0f);
-      key[i] = (static_cast<uint64_t>(score_key(s)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
-    }
+    // at least 1 (only one NaN pattern maps to 0), so with k <= E every
+    // round finds a present expert
+    if (e < E) key[i] = max(score_key(row[e] + (bias ? bias[e] : 0.0f)), 1u);
   }
   int mine = -1;  // lane j < k ends with the j-th selected expert
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    uint32_t best = 0;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max64(best);
-    const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    best = wave_max_u32(best);
+    // lowest expert index holding the key: the first slot i with a match,
+    // then its lowest lane
+    int e = 0;
+#pragma unroll
+    for (int i = NPER - 1; i >= 0; --i) {
+      const uint64_t hit = ballot64(key[i] == best);
+      if (hit) e = i * 64 + __builtin_ctzll(hit);
+    }
     if ((e & 63) == lane) {
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
