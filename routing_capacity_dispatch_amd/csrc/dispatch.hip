@@ -19,6 +19,7 @@ namespace {
 constexpr int kAssignWaves = 16;
 constexpr int kAssignThreads = kAssignWaves * 64;
 constexpr int kChunk = kAssignThreads;  // assignments per block of the slot scan
+constexpr int kRecvBatch = 16;          // id-column loads in flight per lane in receiver binning
 
 __device__ __forceinline__ int key_bits(int n) {  // bits to hold 0..n-1
   int b = 0;
@@ -126,7 +127,18 @@ __global__ __launch_bounds__(kAssignThreads) void assign_slots_kernel(DispatchAr
   const int32_t* cnt = a.chunk_counts + (int64_t)r.w * a.n_chunks * K;
   for (int j = tid; j < K; j += kAssignThreads) {
     int run = 0;
-    for (int c = 0; c < r.c; ++c) run += cnt[(int64_t)c * K + j];
+    {
+      // eight loads in flight at a time
+      int c = 0;
+      for (; c + 8 <= r.c; c += 8) {
+        int x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = cnt[(int64_t)(c + u) * K + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) run += x[u];
+      }
+      for (; c < r.c; ++c) run += cnt[(int64_t)c * K + j];
+    }
     for (int u = 0; u < kAssignWaves; ++u) {
       const int x = wh[u * K + j];
       wh[u * K + j] = run;
@@ -176,13 +188,6 @@ __global__ __launch_bounds__(kAssignThreads) void assign_slots_kernel(DispatchAr
   }
 }
 
-__global__ void finalize_counts_kernel(const int64_t* wave_counts, int W, int64_t* counts) {
-  if (threadIdx.x < 3) {
-    int64_t s = 0;
-    for (int w = 0; w < W; ++w) s += wave_counts[w * 3 + threadIdx.x];
-    counts[threadIdx.x] = s;
-  }
-}
 
 // One wavefront per token: its lanes load the token's k pool slots at once,
 // then the z row is read once and written to every slot the token took.
@@ -205,7 +210,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a, const char
 
 // Receiver side: one wavefront per (wave, pool) block reads only the id
 // column, in slot order, and bins slots to its E/P local experts, keeping the
-// first C_recv of each.
+// first C_recv of each.  The id column is read kRecvBatch x 64 slots at a
+// time (all loads in flight together), then binned 64 slots per step.
 __global__ __launch_bounds__(64) void recv_bin_kernel(DispatchArgs a, int32_t* __restrict__ bank_rows,
                                                       int32_t* __restrict__ expert_count) {
   extern __shared__ int32_t cnt[];  // [E/P]
@@ -215,21 +221,38 @@ __global__ __launch_bounds__(64) void recv_bin_kernel(DispatchArgs a, int32_t* _
   const int epp = E / P;
   const int lbits = key_bits(epp);
   const int cap_send = (int)a.cap_send, cap_recv = (int)a.cap_recv;
+  // the step's kept / sender-dropped / receiver-dropped totals from the slot
+  // scan's per-wave counters (complete: the scan ran in an earlier launch)
+  if (blockIdx.x == 0 && a.counts && lane < 3) {
+    int64_t t = 0;
+    for (int ww = 0; ww < a.W; ++ww) t += a.wave_counts[ww * 3 + lane];
+    a.counts[lane] = t;
+  }
   for (int i = lane; i < epp; i += 64) cnt[i] = 0;
   __syncthreads();
   const int32_t* ids = reinterpret_cast<const int32_t*>(a.pools + ((int64_t)w * P + p) * a.block_bytes + a.ids_offset);
   const uint64_t lt = lanemask_lt();
-  for (int it = 0; it < cap_send; it += 64) {
-    const int s = it + lane;
-    const int id = s < cap_send ? ids[s] : -1;
-    const int le = id - p * epp;
-    const bool valid = id >= 0 && le >= 0 && le < epp;
-    const uint64_t act = ballot64(valid);
-    const uint64_t m = match_key((uint32_t)(valid ? le : 0), lbits, act);
-    int r = 0;
-    if (valid) r = cnt[le] + __popcll(m & lt);
-    if (valid && (m & lt) == 0) cnt[le] = r + __popcll(m);
-    if (valid && r < cap_recv) bank_rows[((int64_t)w * E + id) * cap_recv + r] = s;
+  for (int it0 = 0; it0 < cap_send; it0 += 64 * kRecvBatch) {
+    int idv[kRecvBatch];
+#pragma unroll
+    for (int b = 0; b < kRecvBatch; ++b) {
+      const int s = it0 + b * 64 + lane;
+      idv[b] = s < cap_send ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < kRecvBatch; ++b) {
+      const int s = it0 + b * 64 + lane;
+      const int id = idv[b];
+      const int le = id - p * epp;
+      const bool valid = id >= 0 && le >= 0 && le < epp;
+      const uint64_t act = ballot64(valid);
+      if (!act) continue;  // wave-uniform
+      const uint64_t m = match_key((uint32_t)(valid ? le : 0), lbits, act);
+      int r = 0;
+      if (valid) r = cnt[le] + __popcll(m & lt);
+      if (valid && (m & lt) == 0) cnt[le] = r + __popcll(m);
+      if (valid && r < cap_recv) bank_rows[((int64_t)w * E + id) * cap_recv + r] = s;
+    }
   }
   __syncthreads();
   for (int i = lane; i < epp; i += 64) expert_count[(int64_t)w * E + p * epp + i] = min(cnt[i], cap_recv);
@@ -315,9 +338,6 @@ hipError_t launch_assign(const DispatchArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   assign_slots_kernel<<<grid, kAssignThreads, lds2, s>>>(a);
-  e = hipGetLastError();
-  if (e != hipSuccess || !a.counts) return e;
-  finalize_counts_kernel<<<1, 64, 0, s>>>(a.wave_counts, a.W, a.counts);
   return hipGetLastError();
 }
 
