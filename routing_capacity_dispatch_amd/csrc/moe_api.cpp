@@ -989,7 +989,10 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const BwdRows
   char* DH = static_cast<char*>(cv.take(R * F * 2));
   char* DADB = static_cast<char*>(cv.take(R * 2 * F * 2));
   char* H = static_cast<char*>(cv.take(R * F * 2));
+  // one M-tile structure serves the recompute (expert tile) and dh (dgrad
+  // tile) lists, so the two tiles must have the same row count
   const int bm = moe::bwd_dgrad_rows();
+  if (bm != moe::ragged_tile_rows()) return MOE_ERR_UNSUPPORTED;
   hipError_t e = ragged ? moe::launch_bwd_layout_ragged(src.expert_offsets, E, p.dropless_rows, counts, offsets,
                                                          gidx, s)
                         : moe::launch_bwd_layout(src.bank_rows, src.expert_count, E, c->n_pools, c->n_waves,
