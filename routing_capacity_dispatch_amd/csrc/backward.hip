@@ -121,10 +121,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 }
 
 // Transpose of combine, one wavefront per token t: for each receiver-kept
-// assignment j (dropless: each assignment with a row, row_of >= 0), d_gates[t, j] = <dy[t], o[t, j]> (fp32, lane partial sums
-// in chunk order, then a butterfly over the wavefront) and the row
-// g[t, j] * dy[t] goes to the pool slot the forward read o[t, j] from.  A
-// dropped assignment gets d_gates = 0 and no row.
+// assignment j (dropless: each assignment with a row, row_of >= 0),
+// d_gates[t, j] = <dy[t], o[t, j]> (fp32, lane partial sums in chunk order,
+// then a butterfly over the wavefront) and the row g[t, j] * dy[t] goes to
+// the pool slot the forward read o[t, j] from.  A dropped assignment gets
+// d_gates = 0 and no row.  Lanes j < k load the token's assignments at once;
+// the o rows are then read two at a time.  dy and o are read once, so their
+// loads carry the nontemporal hint.
 template <int kMaxChunks>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -133,47 +136,74 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   const int k = a.k, epp = a.E / a.P;
   const int64_t w = t / a.Tw;
   const int chunks = (int)(a.row_bytes / 16);
-  // dy[t] in registers: chunk c = i * 64 + lane
-  float dy[kMaxChunks][8];
-#pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = i * 64 + lane;
-    if (c < chunks) unpack(ld16(static_cast<const char*>(a.dy) + t * a.row_bytes + (int64_t)c * 16), dy[i], bf16_t{});
-  }
-  for (int j = 0; j < k; ++j) {
-    const int64_t q = t * k + j;
-    int64_t row = -1;
+  int64_t row = -1;
+  float g = 0.0f;
+  if (lane < k) {
+    const int64_t q = t * k + lane;
     if (a.row_of) {  // dropless: the assignment's row in expert order
       row = a.row_of[q];
     } else {
       const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
       if (rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send) row = (w * a.P + e / epp) * a.cap_send + ps;
     }
-    if (row < 0) {
-      if (lane == 0) a.d_gates[q] = 0.0f;
-      continue;
+    if (row >= 0) g = a.gates[q];
+  }
+  // dy[t] in registers: chunk c = i * 64 + lane
+  float dy[kMaxChunks][8];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = i * 64 + lane;
+    if (c < chunks)
+      unpack(ld16_stream(static_cast<const char*>(a.dy) + t * a.row_bytes + (int64_t)c * 16), dy[i], bf16_t{});
+  }
+  float dg = 0.0f;  // lane j < k ends with d_gates[t, j]
+  for (int j = 0; j < k; j += 2) {
+    const int64_t r0 = shfl64(row, j);
+    const int64_t r1 = j + 1 < k ? shfl64(row, j + 1) : -1;
+    const float g0 = __shfl(g, j), g1 = __shfl(g, j + 1);
+    uint4 v0[kMaxChunks], v1[kMaxChunks];
+    const char* o0 = static_cast<const char*>(a.expert_out) + r0 * a.row_bytes;
+    const char* o1 = static_cast<const char*>(a.expert_out) + r1 * a.row_bytes;
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = i * 64 + lane;
+      if (c < chunks && r0 >= 0) v0[i] = ld16_stream(o0 + (int64_t)c * 16);
+      if (c < chunks && r1 >= 0) v1[i] = ld16_stream(o1 + (int64_t)c * 16);
     }
-    const float g = a.gates[q];
-    const char* o = static_cast<const char*>(a.expert_out) + row * a.row_bytes;
-    char* d = static_cast<char*>(a.d_expert_out) + row * a.row_bytes;
-    float s = 0.0f;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxChunks; ++i) {
       const int c = i * 64 + lane;
       if (c >= chunks) continue;
       float f[8], out[8];
-      unpack(ld16(o + (int64_t)c * 16), f, bf16_t{});
+      if (r0 >= 0) {
+        unpack(v0[i], f, bf16_t{});
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        s = fmaf(dy[i][x], f[x], s);
-        out[x] = g * dy[i][x];
+        for (int x = 0; x < 8; ++x) {
+          s0 = fmaf(dy[i][x], f[x], s0);
+          out[x] = g0 * dy[i][x];
+        }
+        st16(static_cast<char*>(a.d_expert_out) + r0 * a.row_bytes + (int64_t)c * 16, pack(out, bf16_t{}));
       }
-      st16(d + (int64_t)c * 16, pack(out, bf16_t{}));
+      if (r1 >= 0) {
+        unpack(v1[i], f, bf16_t{});
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          s1 = fmaf(dy[i][x], f[x], s1);
+          out[x] = g1 * dy[i][x];
+        }
+        st16(static_cast<char*>(a.d_expert_out) + r1 * a.row_bytes + (int64_t)c * 16, pack(out, bf16_t{}));
+      }
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-    if (lane == 0) a.d_gates[q] = s;
+    for (int m = 32; m >= 1; m >>= 1) {
+      s0 += __shfl_xor(s0, m);
+      s1 += __shfl_xor(s1, m);
+    }
+    if (lane == j) dg = r0 >= 0 ? s0 : 0.0f;
+    if (lane == j + 1) dg = r1 >= 0 ? s1 : 0.0f;
   }
+  if (lane < k) a.d_gates[t * k + lane] = dg;
 }
 
 // Softmax backward over the k selected raw logits, one wavefront per token:
