@@ -11,7 +11,9 @@ dropless ragged variant; --backward times the routed path's backward
 (moe_backward_routed, or moe_backward_dropless with --dropless: gate, row and
 weight gradients for one forward call's routing, a seeded dL/dy_latent,
 forward state resident); --bias-update times the router's next-step bias
-update (moe_router_bias_update) on one forward call's logits.
+update (moe_router_bias_update) on one forward call's logits; --recv-share
+times one EP rank's receive share (moe_experts over the capacity-bounded
+bank of 6 local experts, then moe_combine of 65,536 tokens x 8 rows).
 
 Stage durations come from HIP events the library records between its kernel
 launches on the stream it launches them on (moe_forward_profiled), averaged
@@ -249,6 +251,128 @@ def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
             "sample": f"{what}, fp64 numpy, {dt:.1f} s wall, {cores} cores in the affinity mask"}
 
 
+METRIC_SHARE = "MoE receive-share (6 local experts) SwiGLU + combine tokens/sec on 1 MI355X; % bf16 MFMA peak"
+
+
+def bench_recv_share(args):
+    """One EP rank's receive share: the bank of 6 local experts (per wave one
+    block of 6 x 33,497 slots, multinomial loads, id column), moe_experts over
+    all waves' rows, then moe_combine of the rank's 65,536 tokens x 8 rows.
+    A step is both calls; the stages are timed with events on the stream the
+    library launches on (torch's current stream)."""
+    import numpy as np
+    import torch
+
+    import routing_capacity_dispatch_amd as rcd
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    print("# generating the receive-share inputs", file=sys.stderr, flush=True)
+    sh = synth.make_recv_share(seed=args.seed, device=dev)
+    W, n_local, cw, L, F, T, k = (sh[x] for x in ("W", "n_local", "cap_wave", "L", "F", "T", "k"))
+    cfg = rcd.make_config(T, 64, L, n_local, 1, k, F, n_waves=W, dtype="bf16",
+                          cap_send_rows=n_local * cw, cap_recv_rows=cw)
+    p = rcd.plan(cfg)
+    pools = torch.empty(p["pools_bytes"], dtype=torch.uint8, device=dev)
+    rows, ids = rcd.pool_views(cfg, pools)
+    rows[:, 0].copy_(sh["rows"])
+    counts = sh["counts"]
+    slot = torch.arange(n_local * cw, dtype=torch.int32)
+    ids[:, 0].copy_(torch.where((slot % cw)[None, :] < counts.repeat_interleave(cw, dim=1),
+                                (slot // cw)[None, :].expand(W, -1), torch.full_like(slot, -1)[None, :]).to(dev))
+    bank_rows = (torch.arange(n_local, dtype=torch.int32)[:, None] * cw
+                 + torch.arange(cw, dtype=torch.int32)[None, :]).expand(W, -1, -1).contiguous().to(dev)
+    cnt_d = counts.to(dev)
+    expert_of = sh["expert_of"].to(dev)
+    slot_of = sh["slot_of"].to(dev)
+    recv = (sh["slot_of"] % cw).to(torch.int32).to(dev)
+    gates = sh["gates"].to(dev)
+    eo = torch.empty(p["expert_out_bytes"], dtype=torch.uint8, device=dev)
+    y = torch.empty((T, L), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        rcd.experts(cfg, pools, bank_rows, cnt_d, sh["w_gate"], sh["w_up"], sh["w_down"], expert_out=eo)
+        if ev:
+            ev[1].record()
+        rcd.combine(cfg, eo, expert_of, slot_of, recv, gates, y_latent=y)
+        if ev:
+            ev[2].record()
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for row in ev:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    print(f"# timing {K} steps", file=sys.stderr, flush=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(K):
+        step(ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / K
+    ms_exp = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
+    ms_cmb = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
+    n_rows = int(counts.sum())
+    flops = 6.0 * n_rows * L * F           # gate, up and down over the valid rows
+    cbytes = n_rows * L * 2 + T * L * 2 + T * k * 16
+    tf = flops / (ms_exp * 1e-3) / 1e12
+    out = {
+        "metric": METRIC_SHARE, "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "recv_share", "pass": "experts+combine", "T": T, "n_local_experts": n_local,
+                   "d_latent": L, "d_ff": F, "top_k": k, "n_waves": W, "cap_wave_rows": cw,
+                   "valid_rows": n_rows, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_TFLOPS["bf16"], 4), "kernel": "experts (gate/up and down GEMMs)",
+                     "traffic": None},
+        "stages": {"experts": {"ms": round(ms_exp, 4), "tflops": round(tf, 1),
+                               "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)},
+                   "combine": {"ms": round(ms_cmb, 4), "gbs": round(cbytes / (ms_cmb * 1e-3) / 1e9, 1),
+                               "frac_peak": round(cbytes / (ms_cmb * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}},
+        "wall_s_timed": round(wall, 3),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or 32768
+        print(f"# cpu baseline: oracle on the first {n_tok} tokens", file=sys.stderr, flush=True)
+        import oracle
+        ex = sh["expert_of"][:n_tok].numpy()
+        sl = sh["slot_of"][:n_tok].numpy()
+        wv = np.repeat((np.arange(n_tok) // sh["Tw"])[:, None], k, axis=1)
+        u = sh["rows"][torch.from_numpy(wv).to(dev).long(), torch.from_numpy(sl).to(dev).long()]
+        u = u.to("cpu", torch.float32).numpy().astype(np.float64)          # [n_tok, k, L]
+        ws = {int(e): tuple(sh[n][int(e)].to("cpu", torch.float32).numpy().astype(np.float64)
+                            for n in ("w_gate", "w_up", "w_down")) for e in np.unique(ex)}
+        g64 = sh["gates"][:n_tok].numpy().astype(np.float64)
+        t_c = time.perf_counter()
+        o = np.zeros((n_tok, k, L))
+        for e in np.unique(ex):
+            m = ex == e
+            o[m] = oracle.swiglu(u[m], *ws[int(e)])
+        oracle.combine(g64, np.zeros((n_tok, k)), o)
+        dt = time.perf_counter() - t_c
+        out["cpu_baseline"] = {"value": n_tok / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle",
+                               "sample": f"the first {n_tok} tokens' {k} rows each through their experts' SwiGLU "
+                                         f"and the combine, fp64 numpy, {dt:.1f} s wall, "
+                                         f"{len(os.sched_getaffinity(0))} cores in the affinity mask"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +387,9 @@ def main():
     ap.add_argument("--bias-update", action="store_true",
                     help="time the router's next-step bias update (moe_router_bias_update) on one "
                          "forward call's logits instead")
+    ap.add_argument("--recv-share", action="store_true",
+                    help="time one EP rank's receive share instead: moe_experts over 6 local experts "
+                         "(3 wave slabs of 33,497 rows each) then moe_combine of 65,536 tokens x 8")
     ap.add_argument("--bins", type=int, default=256, help="histogram bins of --bias-update")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="oracle sample for the CPU baseline (default 256; 64 with --backward)")
@@ -281,7 +408,7 @@ def main():
     args = ap.parse_args()
     run_name = (args.workload + ("_dropless" if args.dropless else "") + ("_backward" if args.backward else "")
                 + ("_bias" if args.bias_update else ""))
-    if args.cpu_tokens is None:
+    if args.cpu_tokens is None and not args.recv_share:
         args.cpu_tokens = 64 if args.backward else 256
     if args.traffic is None:
         args.traffic = os.path.join(ROOT, "profiles", f"traffic_{run_name}.json")
@@ -295,6 +422,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.recv_share:
+        bench_recv_share(args)
+        return
 
     import torch
 

@@ -17,6 +17,7 @@ namespace {
 constexpr int kSortWaves = 16;
 constexpr int kSortThreads = kSortWaves * 64;
 constexpr int kTileListBlocks = 32;  // workgroups writing the tile lists
+constexpr int kMBand = 8;            // M tiles per band of the expert GEMMs' tile order
 
 __device__ __forceinline__ int key_bits_of(int n) {
   int b = 0;
@@ -156,9 +157,12 @@ __global__ __launch_bounds__(256) void ragged_scatter_kernel(const char* __restr
 
 // Tile lists of the grouped expert GEMMs: expert e gets ceil(rows_e / bm) M
 // tiles; list0 (list1) holds (e, N tile, M tile) for tiles_n0 (tiles_n1) N
-// tiles per M tile, experts in order, then N tiles, then M tiles (M fastest,
-// so the M tiles sharing a weight tile are neighbours).  Every block scans
-// the experts' M-tile counts in LDS, then the grid writes the entries
+// tiles per M tile.  Order: experts in turn; an expert's M tiles in bands of
+// kMBand; within a band the N tiles in turn, each with the band's M tiles
+// (M fastest, so the M tiles sharing a weight tile are neighbours, and a
+// band's rows stay in cache while every N tile reads them).  An expert with
+// at most kMBand M tiles is one band: (N tile, then M tile).  Every block
+// scans the experts' M-tile counts in LDS, then the grid writes the entries
 // (12 bytes each) with consecutive threads on consecutive entries: entry q of
 // a list with tn N tiles belongs to the expert whose M-tile range holds
 // q / tn.
@@ -200,11 +204,14 @@ __global__ __launch_bounds__(1024) void ragged_tiles_kernel(const int32_t* __res
     }
     const int me = first[lo + 1] - first[lo];
     const int rem = (int)(qq - (int64_t)first[lo] * tn);
-    const int nt = rem / me;
+    const int band = rem / (kMBand * tn);                 // full bands come first
+    const int bs = min(kMBand, me - band * kMBand);       // M tiles in this band
+    const int within = rem - band * kMBand * tn;
+    const int nt = within / bs;
     int32_t* d = (one ? list1 : list0) + 3 * qq;
     d[0] = lo;
     d[1] = nt;
-    d[2] = rem - nt * me;
+    d[2] = band * kMBand + (within - nt * bs);
   }
 }
 
