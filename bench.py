@@ -60,7 +60,7 @@ COPY_KERNEL = ("copyBuffer",)
 # sources of the GEMM kernels: a measured traffic figure is used only while
 # they are unchanged
 KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "dispatch.hip",
-                  "gemm_bwd.hip", "backward.hip"]
+                  "gemm_bwd.hip", "backward.hip", "ragged.hip", "route.hip"]
 BIAS_SOURCES = ["bias.hip", "common.h"]
 
 
