@@ -20,6 +20,9 @@ constexpr int kAssignWaves = 16;
 constexpr int kAssignThreads = kAssignWaves * 64;
 constexpr int kChunk = kAssignThreads;  // assignments per block of the slot scan
 constexpr int kRecvBatch = 16;          // id-column loads in flight per lane in receiver binning
+constexpr int kGidxChunk = 2048;        // row-list entries per workgroup of the expert-major row list
+
+inline int64_t ceil_div_i64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 __device__ __forceinline__ int key_bits(int n) {  // bits to hold 0..n-1
   int b = 0;
@@ -297,22 +300,27 @@ __global__ __launch_bounds__(1024) void expert_offsets_kernel(const int32_t* __r
 }
 
 // Flat pool-row index ((w * P + p) * C_send + slot) of every kept row, in
-// expert-major order (waves in order, receiver slots in order).  Counts and
+// expert-major order (waves in order, receiver slots in order).  Workgroup
+// (x, e) writes expert e's list entries [x * kGidxChunk, (x + 1) * kGidxChunk),
+// so an expert with many rows is spread over many workgroups.  Counts and
 // slots are clamped to the block, so malformed lists cannot send the GEMMs
 // outside the pools.
-__global__ __launch_bounds__(64) void expert_gidx_kernel(const int32_t* __restrict__ bank_rows,
-                                                         const int32_t* __restrict__ expert_count,
-                                                         const int32_t* __restrict__ offsets, int E, int P, int W,
-                                                         int cap_send, int cap_recv, int32_t* __restrict__ gidx) {
-  const int e = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void expert_gidx_kernel(const int32_t* __restrict__ bank_rows,
+                                                          const int32_t* __restrict__ expert_count,
+                                                          const int32_t* __restrict__ offsets, int E, int P, int W,
+                                                          int cap_send, int cap_recv, int32_t* __restrict__ gidx) {
+  const int e = blockIdx.y;
   const int p = e / (E / P);
-  int off = offsets[e];
-  for (int w = 0; w < W; ++w) {
+  const int lo = blockIdx.x * kGidxChunk, hi = lo + kGidxChunk;
+  const int off = offsets[e];
+  int pre = 0;  // the expert's rows in earlier waves
+  for (int w = 0; w < W && pre < hi; ++w) {
     const int c = min(max(expert_count[(int64_t)w * E + e], 0), cap_recv);
-    const int32_t* br = bank_rows + ((int64_t)w * E + e) * cap_recv;
+    const int a = max(lo, pre), b = min(hi, pre + c);
+    const int32_t* br = bank_rows + ((int64_t)w * E + e) * cap_recv - pre;
     const int base = (w * P + p) * cap_send;
-    for (int r = lane; r < c; r += 64) gidx[off + r] = base + min(max(br[r], 0), cap_send - 1);
-    off += c;
+    for (int i = a + (int)threadIdx.x; i < b; i += 256) gidx[off + i] = base + min(max(br[i], 0), cap_send - 1);
+    pre += c;
   }
 }
 
@@ -368,8 +376,10 @@ hipError_t launch_expert_gidx(const int32_t* bank_rows, const int32_t* expert_co
   expert_offsets_kernel<<<1, 1024, 0, s>>>(expert_count, E, W, (int)cap_recv, offsets);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  expert_gidx_kernel<<<E, 64, 0, s>>>(bank_rows, expert_count, offsets, E, P, W, (int)cap_send, (int)cap_recv,
-                                      gidx);
+  if ((int64_t)W * cap_recv <= 0 || E <= 0) return hipSuccess;  // no kept rows: the list is empty
+  const dim3 grid((unsigned)ceil_div_i64((int64_t)W * cap_recv, kGidxChunk), (unsigned)E);
+  expert_gidx_kernel<<<grid, 256, 0, s>>>(bank_rows, expert_count, offsets, E, P, W, (int)cap_send, (int)cap_recv,
+                                          gidx);
   return hipGetLastError();
 }
 
