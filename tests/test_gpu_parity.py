@@ -190,6 +190,11 @@ EXPERT_CASES = [
     ("mid_bf16", 4096, 64, 16, 8, 3, 512, 512, "bf16", 0.01),
     ("ragged", 333, 12, 4, 3, 2, 192, 320, "bf16", 0.2),
     ("marin", 16384, 384, 64, 8, 3, 3072, 3072, "bf16", 0.0),
+    # few experts with many rows: 11 M tiles of 192 rows per expert (a band of
+    # 8 M tiles, then a partial band of 3) ...
+    ("bands", 4096, 2, 1, 1, 1, 256, 256, "bf16", 0.0),
+    # ... and 12, 18 and 16 M tiles over three waves, with receiver drops
+    ("bands_w3", 9000, 3, 1, 1, 3, 128, 256, "bf16", 0.3),
 ]
 
 
