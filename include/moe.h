@@ -25,7 +25,9 @@
  * Conventions for every entry point
  *   - Pointers marked (device) are device memory owned by the caller; the
  *     library never allocates, frees, or keeps them.  Pointers marked (host)
- *     are read during the call only.
+ *     are read during the call only.  A buffer whose size in the plan is 0
+ *     (the pools, expert outputs and their gradients when the sender
+ *     capacity is 0; bank_rows when the receiver capacity is 0) may be NULL.
  *   - Matrices are row-major.  Weights are [out, in] (the torch.nn.Linear
  *     layout): y = x W^T, so every contraction reads both operands along
  *     their contiguous dimension.

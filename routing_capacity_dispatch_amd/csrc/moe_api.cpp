@@ -559,7 +559,9 @@ MOE_API moe_status moe_combine(const moe_config* cfg, const void* expert_out,
   moe_plan p;
   moe_status st = plan_impl(cfg, &p);
   if (st != MOE_OK) return st;
-  if (cfg->T > 0 && (!expert_out || !topk_idx || !pool_slot || !recv_slot || !gates || !y_latent))
+  // pool-shaped buffers are empty when the sender capacity is 0: then they may be null
+  if (cfg->T > 0 && ((p.expert_out_bytes > 0 && !expert_out) || !topk_idx || !pool_slot || !recv_slot || !gates ||
+                     !y_latent))
     return MOE_ERR_INVALID_ARG;
   return run_combine(cfg, p, expert_out, topk_idx, pool_slot, recv_slot, gates, y_latent,
                      static_cast<hipStream_t>(stream));
@@ -1114,8 +1116,10 @@ moe_status backward_impl(const moe_config* cfg, const moe_weights* w, const moe_
   moe_plan p;
   moe_status st = check_backward(cfg, &p);
   if (st != MOE_OK) return st;
-  if (!w || !sv || !w->w_gate || !w->w_up || !w->w_down || !dwg || !dwu || !dwd || !sv->expert_count ||
-      !sv->bank_rows || !sv->pools || !sv->expert_out)
+  if (!w || !sv || !w->w_gate || !w->w_up || !w->w_down || !dwg || !dwu || !dwd || !sv->expert_count)
+    return MOE_ERR_INVALID_ARG;
+  // pool-shaped buffers are empty when a capacity is 0: then they may be null
+  if ((p.pools_bytes > 0 && (!sv->pools || !sv->expert_out)) || (p.cap_recv > 0 && !sv->bank_rows))
     return MOE_ERR_INVALID_ARG;
   if (cfg->T > 0 && (!sv->topk_idx || !sv->gates || !sv->pool_slot || !sv->recv_slot || !dy || !dz || !d_logits))
     return MOE_ERR_INVALID_ARG;
@@ -1155,8 +1159,8 @@ MOE_API moe_status moe_combine_backward(const moe_config* cfg, const void* exper
   moe_plan p;
   moe_status st = check_backward(cfg, &p);
   if (st != MOE_OK) return st;
-  if (cfg->T > 0 && (!expert_out || !topk_idx || !pool_slot || !recv_slot || !gates || !dy_latent || !d_gates ||
-                     !d_expert_out))
+  if (cfg->T > 0 && ((p.expert_out_bytes > 0 && (!expert_out || !d_expert_out)) || !topk_idx || !pool_slot ||
+                     !recv_slot || !gates || !dy_latent || !d_gates))
     return MOE_ERR_INVALID_ARG;
   return run_combine_bwd(cfg, p, expert_out, topk_idx, pool_slot, recv_slot, gates, dy_latent, d_gates,
                          d_expert_out, static_cast<hipStream_t>(stream));
@@ -1170,8 +1174,8 @@ MOE_API moe_status moe_experts_backward(const moe_config* cfg, const void* pools
   moe_plan p;
   moe_status st = check_backward(cfg, &p);
   if (st != MOE_OK) return st;
-  if (!expert_count || !bank_rows || !pools || !d_expert_out || !d_pool_rows || !w_gate || !w_up || !w_down ||
-      !dw_gate || !dw_up || !dw_down)
+  if (!expert_count || !w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down) return MOE_ERR_INVALID_ARG;
+  if ((p.pools_bytes > 0 && (!pools || !d_expert_out || !d_pool_rows)) || (p.cap_recv > 0 && !bank_rows))
     return MOE_ERR_INVALID_ARG;
   if (!ws || (int64_t)ws_bytes < p.experts_bwd_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
   const BwdRows src{bank_rows, expert_count, nullptr, pools, d_expert_out, d_pool_rows};
@@ -1185,7 +1189,8 @@ MOE_API moe_status moe_dispatch_backward(const moe_config* cfg, const int32_t* t
   moe_plan p;
   moe_status st = check_backward(cfg, &p);
   if (st != MOE_OK) return st;
-  if (cfg->T > 0 && (!topk_idx || !pool_slot || !recv_slot || !d_pool_rows || !dz)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!topk_idx || !pool_slot || !recv_slot || (p.expert_out_bytes > 0 && !d_pool_rows) || !dz))
+    return MOE_ERR_INVALID_ARG;
   return run_dispatch_bwd(cfg, p, topk_idx, pool_slot, recv_slot, d_pool_rows, dz,
                           static_cast<hipStream_t>(stream));
 }

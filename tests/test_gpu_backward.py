@@ -45,6 +45,8 @@ def _saved_o(cfg, fwd, toks=None):
     topk = np_i(taps["topk_idx"])[toks]
     ps = np_i(taps["pool_slot"])[toks]
     keep = np_i(taps["recv_slot"])[toks] >= 0
+    if not keep.any():  # nothing kept (e.g. a zero capacity: the buffer may be empty)
+        return np.zeros((len(toks), k, L))
     w = toks[:, None] // p["tokens_per_wave"]
     row = (w * cfg.n_pools + topk // (cfg.n_experts // cfg.n_pools)) * p["cap_send"] + np.maximum(ps, 0)
     eo = rcd.expert_out_view(cfg, taps["expert_out"]).reshape(-1, L)
@@ -94,7 +96,9 @@ def test_backward_routed_mid(seed):
 
 
 @pytest.mark.parametrize("over", [dict(recv_cap=(1, 2)), dict(send_cap=(1, 2)), dict(n_waves=1),
-                                  dict(n_pools=1), dict(top_k=1), dict(top_k=2, T=1000)])
+                                  dict(n_pools=1), dict(top_k=1), dict(top_k=2, T=1000),
+                                  # every assignment dropped: zero-size pools (null buffers), zero gradients
+                                  dict(send_cap=(0, 1)), dict(recv_cap=(0, 1))])
 def test_backward_routed_special_cases(over):
     d = dev()
     say("backward special", over)
