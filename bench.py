@@ -42,13 +42,13 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 kernel names of the stages (substrings that all must match)
 STAGE_KERNEL = {
     "latent": ("dense1_bf16_kernel",),
-    "expert_gate_up": ("ragged_gemm_kernel", ", 1>"),
-    "expert_down": ("ragged_gemm_kernel", ", 0>"),
+    "expert_gate_up": ("ragged_gemm_kernel", ">, 1>("),
+    "expert_down": ("ragged_gemm_kernel", ">, 0>("),
     "shared_gate_up": ("swiglu_bf16_kernel",),
     "output": ("dense_bf16_kernel",),
     "combine": ("combine_kernel",),
     "scatter": ("scatter_kernel",),
-    "swiglu_bwd": ("ragged_gemm_kernel", ", 2>"),
+    "swiglu_bwd": ("ragged_gemm_kernel", ">, 2>("),
     "dh": ("dgrad_kernel", "<0>"),
     "du": ("dgrad_kernel", "<1>"),
     "dw_down": ("wgrad_kernel",),
