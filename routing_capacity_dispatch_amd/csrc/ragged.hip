@@ -51,8 +51,18 @@ __global__ __launch_bounds__(1024) void ragged_scan_kernel(const int32_t* __rest
   __shared__ int32_t part[16];
   const int e = threadIdx.x;
   int run = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) run += hist[(int64_t)b * E + e];
+  if (e < E) {
+    // eight loads in flight at a time
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      int x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) run += x[u];
+    }
+    for (; b < nblk; ++b) run += hist[(int64_t)b * E + e];
+  }
   tot[e] = e < E ? run : 0;
   __syncthreads();
   // exclusive scan of tot[0..1023]: per wavefront, then across wavefronts
@@ -78,7 +88,18 @@ __global__ __launch_bounds__(1024) void ragged_scan_kernel(const int32_t* __rest
   if (e < E) {
     offsets[e] = excl;
     int r = excl;
-    for (int b = 0; b < nblk; ++b) {
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      int x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        base[(int64_t)(b + u) * E + e] = r;
+        r += x[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       base[(int64_t)b * E + e] = r;
       r += hist[(int64_t)b * E + e];
     }
