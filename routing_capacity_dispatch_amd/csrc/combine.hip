@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       g = a.gates ? a.gates[q] : 1.0f;
     }
   }
-  combine_rows<T>(a.expert_out, row, g, k, a.row_bytes, static_cast<char*>(a.y) + t * a.row_bytes);
+  combine_rows<T>(a.expert_out, row, g, k, a.row_bytes,
+                  static_cast<char*>(a.y) + t * (a.y_pitch ? a.y_pitch : a.row_bytes));
 }
 
 }  // namespace

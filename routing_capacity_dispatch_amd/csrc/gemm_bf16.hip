@@ -164,9 +164,35 @@ __global__ __launch_bounds__(DenseTile::THREADS) void dense_bf16_kernel(GemmDens
                 [&](int r) { return C + ((int64_t)(m0 + r) * g.ldc + n0) * 2; });
 }
 
-// One K range (the latent projection): the mid-tile barrier schedule with a
-// third B stage.  A few registers spill around the K loop, none inside it.
-__global__ __launch_bounds__(DenseTile3B::THREADS) void dense1_bf16_kernel(GemmDense g, int tiles_m, int tiles_n) {
+// K ranges whose A parts are consecutive columns of one row-major buffer
+// and whose B parts are separate arrays of one row pitch (the output
+// projection over [y_lat | shared hidden rows]): A is one operand, B's K
+// tile j comes from the range holding it.
+struct SegK {
+  static constexpr bool kLinear = false;
+  const char* p[kMaxSegs];
+  int first[kMaxSegs];  // first K tile of each range
+  int n;
+  __device__ __forceinline__ const char* operator()(const char*, int j, int64_t kstep) const {
+    const char* q = p[0];
+    int f = 0;
+#pragma unroll
+    for (int s = 1; s < kMaxSegs; ++s)
+      if (s < n && j >= first[s]) {
+        q = p[s];
+        f = first[s];
+      }
+    return q + (int64_t)(j - f) * kstep;
+  }
+};
+
+// One K range (the latent projection), or K ranges joined as SegK
+// describes (Seg = true: ktiles K tiles over all of them; the one-range
+// kernel reads its K from the segment): the mid-tile barrier schedule with
+// a third B stage.  A few registers spill around the K loop, none inside it.
+template <bool Seg>
+__device__ __forceinline__ void dense1_body(const GemmDense& g, const SegK& bk, int ktiles, int tiles_m,
+                                            int tiles_n) {
   using TL = DenseTile3B;
   __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
   const int t = xcd_order(blockIdx.x, gridDim.x);
@@ -194,7 +220,10 @@ __global__ __launch_bounds__(DenseTile3B::THREADS) void dense1_bf16_kernel(GemmD
   }
   Acc<TL> acc;
   acc.zero();
-  mainloop<TL>(a_src, b_src, sg.K / TL::BK, lds, acc);
+  if constexpr (Seg)
+    mainloop<TL, true, false, false, SegK>(a_src, b_src, ktiles, lds, acc, TL::RB, TL::RB, bk);
+  else
+    mainloop<TL>(a_src, b_src, sg.K / TL::BK, lds, acc);
   constexpr int ld = TL::BN * 2 + kStagePad;
   stage_bf16<TL>(acc, lds, ld);
   __syncthreads();
@@ -202,6 +231,15 @@ __global__ __launch_bounds__(DenseTile3B::THREADS) void dense1_bf16_kernel(GemmD
   char* C = static_cast<char*>(g.C);
   copy_rows<TL>(lds, ld, cpr, min(TL::BM, g.M - m0), min(cpr, (g.N - n0) * 2 / 16),
                 [&](int r) { return C + ((int64_t)(m0 + r) * g.ldc + n0) * 2; });
+}
+
+__global__ __launch_bounds__(DenseTile3B::THREADS) void dense1_bf16_kernel(GemmDense g, int tiles_m, int tiles_n) {
+  dense1_body<false>(g, SegK{}, 0, tiles_m, tiles_n);
+}
+
+__global__ __launch_bounds__(DenseTile3B::THREADS) void densecat_bf16_kernel(GemmDense g, SegK bk, int ktiles,
+                                                                           int tiles_m, int tiles_n) {
+  dense1_body<true>(g, bk, ktiles, tiles_m, tiles_n);
 }
 
 // bf16 operands, fp32 output, one K range (the router logits).
@@ -484,11 +522,39 @@ hipError_t launch_ragged_swiglu_bwd_bf16(const RaggedGemm& g, int64_t max_entrie
   return hipGetLastError();
 }
 
+// K ranges that can run as one: A parts consecutive columns of one buffer
+// with one row pitch, B parts of one row pitch, whole K tiles in each.
+bool joinable_segments(const GemmDense& g, SegK& bk, int& ktiles) {
+  if (g.nseg < 2 || g.nseg > kMaxSegs) return false;
+  const char* a0 = static_cast<const char*>(g.seg[0].A);
+  int64_t k = 0;
+  for (int s = 0; s < g.nseg; ++s) {
+    const GemmSeg& q = g.seg[s];
+    if (q.lda != g.seg[0].lda || q.ldb != g.seg[0].ldb || q.K <= 0 || q.K % DenseTile3B::BK) return false;
+    if (static_cast<const char*>(q.A) != a0 + k * 2) return false;
+    bk.p[s] = static_cast<const char*>(q.B);
+    bk.first[s] = (int)(k / DenseTile3B::BK);
+    k += q.K;
+  }
+  if (k > g.seg[0].lda) return false;
+  for (int s = g.nseg; s < kMaxSegs; ++s) {
+    bk.p[s] = bk.p[0];
+    bk.first[s] = (int)(k / DenseTile3B::BK);
+  }
+  bk.n = g.nseg;
+  ktiles = (int)(k / DenseTile3B::BK);
+  return true;
+}
+
 hipError_t launch_gemm_dense_bf16(const GemmDense& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int tm = cdiv(g.M, DenseTile::BM), tn = cdiv(g.N, DenseTile::BN);
+  SegK bk{};
+  int ktiles = 0;
   if (g.nseg == 1)
     dense1_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile3B::THREADS, 0, s>>>(g, tm, tn);
+  else if (joinable_segments(g, bk, ktiles))
+    densecat_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile3B::THREADS, 0, s>>>(g, bk, ktiles, tm, tn);
   else
     dense_bf16_kernel<<<pad8((int64_t)tm * tn), DenseTile::THREADS, 0, s>>>(g, tm, tn);
   return hipGetLastError();

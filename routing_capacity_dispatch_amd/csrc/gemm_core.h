@@ -112,6 +112,16 @@ struct Acc {
   }
 };
 
+// Address of K tile j of a row source: tiles follow one another at `kstep`
+// bytes from the source's base (every operand but the split output
+// projection's weights, whose K ranges sit in separate arrays).
+struct LinearK {
+  static constexpr bool kLinear = true;
+  __device__ __forceinline__ const char* operator()(const char* base, int j, int64_t kstep) const {
+    return base + j * kstep;
+  }
+};
+
 // Issue the loads of one K tile of A or B into one stage: row sources
 // advanced by `koff` bytes (wave-uniform).
 template <class TL, int N>
@@ -371,10 +381,14 @@ __device__ __forceinline__ void wait_loads() {
 // kSplit selects the mid-tile barrier schedule (64-wide K tiles, 2 A
 // stages); it holds two fragment sets live, so kernels short of registers
 // take the plain schedule.
-template <class TL, bool kSplit = true, bool AK = false, bool BK = false>
+// bp maps (B base, K tile index, b_kstep) to the tile's address; only the
+// split schedule takes a policy other than LinearK.
+template <class TL, bool kSplit = true, bool AK = false, bool BK = false, class BP = LinearK>
 __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const RowSrc<TL::B_INS>& b_src,
                                          int ktiles, char* lds,
-                                         Acc<TL>& acc, int64_t a_kstep = TL::RB, int64_t b_kstep = TL::RB) {
+                                         Acc<TL>& acc, int64_t a_kstep = TL::RB, int64_t b_kstep = TL::RB,
+                                         BP bp = BP()) {
+  static_assert(BP::kLinear || (kSplit && TL::KS == 2 && TL::NS == 2), "B tile policy needs the split schedule");
   constexpr int P = TL::A_INS + TL::B_INS;  // load instructions per tile per wavefront
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
@@ -392,13 +406,29 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
     // Issue order: A0 B0 A1 B1 [B2] | A2 B(NSB) | A3 B(NSB+1) | ...
     constexpr int PB = TL::B_INS;
     constexpr int DB = TL::NSB - 1;  // B tiles issued ahead
-    issue_rows<TL>(a_src, 0, lds_a, wave);
-    issue_rows<TL>(b_src, 0, lds_b, wave);
-    if (ktiles > 1) {
-      issue_rows<TL>(a_src, a_kstep, lds_a + TL::A_BYTES, wave);
-      issue_rows<TL>(b_src, b_kstep, lds_b + TL::B_BYTES, wave);
+    // B tile j into a stage (LinearK: the row sources advanced j K steps)
+    auto issue_b = [&](int j, char* stage) {
+#pragma unroll
+      for (int i = 0; i < TL::B_INS; ++i)
+        lds_load16(bp(b_src.base[i], j, b_kstep), b_src.off[i], stage + (i * TL::NW + wave) * 1024);
+    };
+    if constexpr (BP::kLinear) {
+      issue_rows<TL>(a_src, 0, lds_a, wave);
+      issue_rows<TL>(b_src, 0, lds_b, wave);
+      if (ktiles > 1) {
+        issue_rows<TL>(a_src, a_kstep, lds_a + TL::A_BYTES, wave);
+        issue_rows<TL>(b_src, b_kstep, lds_b + TL::B_BYTES, wave);
+      }
+      if (DB == 2 && ktiles > 2) issue_rows<TL>(b_src, 2 * b_kstep, lds_b + 2 * TL::B_BYTES, wave);
+    } else {
+      issue_rows<TL>(a_src, 0, lds_a, wave);
+      issue_b(0, lds_b);
+      if (ktiles > 1) {
+        issue_rows<TL>(a_src, a_kstep, lds_a + TL::A_BYTES, wave);
+        issue_b(1, lds_b + TL::B_BYTES);
+      }
+      if (DB == 2 && ktiles > 2) issue_b(2, lds_b + 2 * TL::B_BYTES);
     }
-    if (DB == 2 && ktiles > 2) issue_rows<TL>(b_src, 2 * b_kstep, lds_b + 2 * TL::B_BYTES, wave);
     if (DB == 2 && ktiles > 2)
       wait_loads<P + PB>();
     else if (ktiles > 1)
@@ -428,6 +458,7 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
       set_prio<1>();
       // tile kt's stages are free: they take A(kt+2) and B(kt+NSB)
       const int64_t ka = (kt + 2) * a_kstep, kb = (kt + TL::NSB) * b_kstep;
+      const int jb = kt + TL::NSB;
       char* da = lds_a + (kt & 1) * TL::A_BYTES + wave * 1024;
       char* db = lds_b + sb * TL::B_BYTES + wave * 1024;
       mfma_read_issue<TL, TL::A_INS + TL::B_INS, AK, BK>(
@@ -435,7 +466,8 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
             if (s < TL::A_INS)
               lds_load16(a_src.base[s] + ka, a_src.off[s], da + s * TL::NW * 1024);
             else
-              lds_load16(b_src.base[s - TL::A_INS] + kb, b_src.off[s - TL::A_INS],
+              lds_load16(BP::kLinear ? b_src.base[s - TL::A_INS] + kb : bp(b_src.base[s - TL::A_INS], jb, b_kstep),
+                         b_src.off[s - TL::A_INS],
                          db + (s - TL::A_INS) * TL::NW * 1024);
           });
       set_prio<0>();
@@ -451,8 +483,12 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
       else
         wait_loads<0>();
       if (kt + 2 < ktiles) issue_rows<TL>(a_src, (kt + 2) * a_kstep, lds_a + (kt & 1) * TL::A_BYTES, wave);
-      if (kt + TL::NSB < ktiles)
-        issue_rows<TL>(b_src, (kt + TL::NSB) * b_kstep, lds_b + sb * TL::B_BYTES, wave);
+      if (kt + TL::NSB < ktiles) {
+        if constexpr (BP::kLinear)
+          issue_rows<TL>(b_src, (kt + TL::NSB) * b_kstep, lds_b + sb * TL::B_BYTES, wave);
+        else
+          issue_b(kt + TL::NSB, lds_b + sb * TL::B_BYTES);
+      }
       mfma_and_read<TL, AK, BK>(f1, acc, lds_a + ((kt + 1) & 1) * TL::A_BYTES, lds_b + sb1 * TL::B_BYTES, 0, f0, wm, wn,
                         lane);
       sb = sb1;

@@ -130,6 +130,7 @@ struct CombineArgs {
   int k, E, P;
   int64_t cap_send, row_bytes;
   void* y;
+  int64_t y_pitch;  // bytes between output rows; 0: row_bytes
 };
 hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s);
 
@@ -148,8 +149,9 @@ hipError_t launch_ragged_scatter(const void* z, const int32_t* row_of, int64_t T
 // triples, M tiles of bm rows; ntiles[0], ntiles[1] = entries of each list.
 hipError_t launch_ragged_tiles(const int32_t* offsets, int E, int bm, int tiles_n0, int tiles_n1,
                                int32_t* list0, int32_t* list1, int32_t* ntiles, hipStream_t s);
+// y_pitch: bytes between output rows (0: row_bytes)
 hipError_t launch_ragged_combine(int dt, const void* out, const int32_t* row_of, const float* gates, int64_t T,
-                                 int k, int64_t row_bytes, void* y, hipStream_t s);
+                                 int k, int64_t row_bytes, void* y, hipStream_t s, int64_t y_pitch = 0);
 
 // Ragged grouped GEMMs (bf16, gemm_bf16.hip).  Expert e's rows are rows
 // [offsets[e], offsets[e+1]) of A and of C.

@@ -431,7 +431,7 @@ moe_status run_experts(const moe_config* c, const moe_plan& p, const void* pools
 
 moe_status run_combine(const moe_config* c, const moe_plan& p, const void* expert_out,
                        const int32_t* topk, const int32_t* pool_slot, const int32_t* recv_slot,
-                       const float* gates, void* y_latent, hipStream_t s) {
+                       const float* gates, void* y_latent, hipStream_t s, int64_t y_pitch = 0) {
   moe::CombineArgs a{};
   a.expert_out = static_cast<const char*>(expert_out);
   a.topk = topk;
@@ -446,6 +446,7 @@ moe_status run_combine(const moe_config* c, const moe_plan& p, const void* exper
   a.cap_send = p.cap_send;
   a.row_bytes = p.row_bytes;
   a.y = y_latent;
+  a.y_pitch = y_pitch;
   return hip_status(moe::launch_combine(c->dtype, a, s));
 }
 
@@ -612,6 +613,15 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const void*
   void* expert_out = pick(tp.expert_out, p.expert_out_bytes);
   void* y_lat = pick(tp.y_latent, T * L * eb);
   void* hs = cv.take(T * S * Fs * eb);
+  // Without a y_latent tap, y_lat and the shared hidden rows are the two
+  // column blocks of one [T][L + S*Fs] buffer (it fits in the two carves
+  // above), so the output projection reads one A operand over all its K
+  // ranges.
+  int64_t ylat_ld = L, hs_ld = S * Fs;
+  if (!tp.y_latent && S > 0 && T * (L + S * Fs) * eb < (int64_t(1) << 32)) {
+    hs = static_cast<char*>(y_lat) + L * eb;
+    ylat_ld = hs_ld = L + S * Fs;
+  }
   int64_t* cnt = static_cast<int64_t*>(pick(counts, 3 * 8));
   void* dws = cv.take(p.dispatch_ws_bytes);
   void* xws = cv.take(p.experts_ws_bytes);
@@ -648,22 +658,22 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const void*
   st = run_experts(cfg, p, pools, bank_rows, expert_count, w->w_gate, w->w_up, w->w_down,
                    expert_out, xws, s, m);
   if (st != MOE_OK) return st;
-  st = run_combine(cfg, p, expert_out, topk, pool_slot, recv_slot, gates, y_lat, s);
+  st = run_combine(cfg, p, expert_out, topk, pool_slot, recv_slot, gates, y_lat, s, ylat_ld * eb);
   if (st == MOE_OK && m->mark(s) != hipSuccess) st = MOE_ERR_HIP;
   if (st != MOE_OK) return st;
   // shared experts' hidden rows: silu(x Wg_s^T) * (x Wu_s^T), [T][S*Fs]
   if (S > 0) {
     e = moe::launch_swiglu_dense(dt, x, D, w->ws_gate, w->ws_up, (int)S, (int)Fs, (int)D, (int)T,
-                                 hs, S * Fs, s);
+                                 hs, hs_ld, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (m->mark(s) != hipSuccess) return MOE_ERR_HIP;
   // y = y_lat W_up^T + sum_s hs_s Wd_s^T: one accumulation over K segments
   moe::GemmDense o{};
   o.nseg = 1 + (int)S;
-  o.seg[0] = {y_lat, L, w->w_up_proj, L, (int)L};
+  o.seg[0] = {y_lat, ylat_ld, w->w_up_proj, L, (int)L};
   for (int sh = 0; sh < S; ++sh)
-    o.seg[1 + sh] = {static_cast<const char*>(hs) + sh * Fs * eb, S * Fs,
+    o.seg[1 + sh] = {static_cast<const char*>(hs) + sh * Fs * eb, hs_ld,
                      static_cast<const char*>(w->ws_down) + sh * D * Fs * eb, Fs, (int)Fs};
   o.C = y;
   o.ldc = D;
@@ -812,6 +822,15 @@ moe_status forward_dropless_impl(const moe_config* cfg, const moe_weights* w, co
   void* out = pick(tp.expert_out, n * L * eb);
   void* y_lat = pick(tp.y_latent, T * L * eb);
   void* hs = cv.take(T * S * Fs * eb);
+  // Without a y_latent tap, y_lat and the shared hidden rows are the two
+  // column blocks of one [T][L + S*Fs] buffer (it fits in the two carves
+  // above), so the output projection reads one A operand over all its K
+  // ranges.
+  int64_t ylat_ld = L, hs_ld = S * Fs;
+  if (!tp.y_latent && S > 0 && T * (L + S * Fs) * eb < (int64_t(1) << 32)) {
+    hs = static_cast<char*>(y_lat) + L * eb;
+    ylat_ld = hs_ld = L + S * Fs;
+  }
   int64_t* cnt = static_cast<int64_t*>(pick(counts, 3 * 8));
   void* dws = cv.take(p.dropless_dispatch_ws_bytes);
   void* xws = cv.take(p.dropless_experts_ws_bytes);
@@ -844,20 +863,20 @@ moe_status forward_dropless_impl(const moe_config* cfg, const moe_weights* w, co
   if (st != MOE_OK) return st;
   st = run_experts_dropless(cfg, p, xs, offsets, w->w_gate, w->w_up, w->w_down, out, xws, s, m);
   if (st != MOE_OK) return st;
-  e = moe::launch_ragged_combine(dt, out, row_of, gates, T, (int)k, p.row_bytes, y_lat, s);
+  e = moe::launch_ragged_combine(dt, out, row_of, gates, T, (int)k, p.row_bytes, y_lat, s, ylat_ld * eb);
   if (e == hipSuccess) e = m->mark(s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (S > 0) {
-    e = moe::launch_swiglu_dense(dt, x, D, w->ws_gate, w->ws_up, (int)S, (int)Fs, (int)D, (int)T, hs, S * Fs,
+    e = moe::launch_swiglu_dense(dt, x, D, w->ws_gate, w->ws_up, (int)S, (int)Fs, (int)D, (int)T, hs, hs_ld,
                                  s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (m->mark(s) != hipSuccess) return MOE_ERR_HIP;
   moe::GemmDense o{};
   o.nseg = 1 + (int)S;
-  o.seg[0] = {y_lat, L, w->w_up_proj, L, (int)L};
+  o.seg[0] = {y_lat, ylat_ld, w->w_up_proj, L, (int)L};
   for (int sh = 0; sh < S; ++sh)
-    o.seg[1 + sh] = {static_cast<const char*>(hs) + sh * Fs * eb, S * Fs,
+    o.seg[1 + sh] = {static_cast<const char*>(hs) + sh * Fs * eb, hs_ld,
                      static_cast<const char*>(w->ws_down) + sh * D * Fs * eb, Fs, (int)Fs};
   o.C = y;
   o.ldc = D;

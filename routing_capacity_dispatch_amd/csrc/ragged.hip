@@ -243,7 +243,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void ragged_combine_kernel(const char* __restrict__ out,
                                                               const int32_t* __restrict__ row_of,
                                                               const float* __restrict__ gates, int64_t Tn, int k,
-                                                              int64_t row_bytes, char* __restrict__ y) {
+                                                              int64_t row_bytes, char* __restrict__ y,
+                                                              int64_t y_pitch) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void ragged_combine_kernel(const char* __restr
     row = row_of[t * k + lane];
     if (row >= 0) g = gates ? gates[t * k + lane] : 1.0f;
   }
-  combine_rows<T>(out, row, g, k, row_bytes, y + t * row_bytes);
+  combine_rows<T>(out, row, g, k, row_bytes, y + t * y_pitch);
 }
 
 }  // namespace
@@ -296,15 +297,16 @@ hipError_t launch_ragged_tiles(const int32_t* offsets, int E, int bm, int tiles_
 }
 
 hipError_t launch_ragged_combine(int dt, const void* out, const int32_t* row_of, const float* gates, int64_t T,
-                                 int k, int64_t row_bytes, void* y, hipStream_t s) {
+                                 int k, int64_t row_bytes, void* y, hipStream_t s, int64_t y_pitch) {
   if (T <= 0) return hipSuccess;
+  if (y_pitch == 0) y_pitch = row_bytes;
   const unsigned blocks = (unsigned)((T + 3) / 4);
   const char* o = static_cast<const char*>(out);
   char* yy = static_cast<char*>(y);
   if (dt == DT_BF16)
-    ragged_combine_kernel<bf16_t><<<blocks, 256, 0, s>>>(o, row_of, gates, T, k, row_bytes, yy);
+    ragged_combine_kernel<bf16_t><<<blocks, 256, 0, s>>>(o, row_of, gates, T, k, row_bytes, yy, y_pitch);
   else
-    ragged_combine_kernel<float><<<blocks, 256, 0, s>>>(o, row_of, gates, T, k, row_bytes, yy);
+    ragged_combine_kernel<float><<<blocks, 256, 0, s>>>(o, row_of, gates, T, k, row_bytes, yy, y_pitch);
   return hipGetLastError();
 }
 

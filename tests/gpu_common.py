@@ -41,3 +41,16 @@ def bank_valid(bank_rows, expert_count):
     W, E, C = bank_rows.shape
     r = np.arange(C)[None, None, :]
     return np.where(r < expert_count[:, :, None], bank_rows, -1)
+
+
+def check_untapped(fwd, cfg, weights, x, y_tapped):
+    # Without taps, y_lat and the shared hidden rows share one buffer and the
+    # output projection runs as one K range (bf16 with d_latent == d_ff_shared:
+    # the joined-range kernel); with taps they are separate K ranges.  Both
+    # accumulate every output in the same K order, so y is the same bits.
+    y2, _, _ = fwd(cfg, weights, x)
+    torch.cuda.synchronize()
+    a, b = y_tapped, y2
+    if a.dtype == torch.bfloat16:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    assert torch.equal(a, b)

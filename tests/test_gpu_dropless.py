@@ -12,7 +12,7 @@ import oracle
 import routing_capacity_dispatch_amd as rcd
 import synth
 from _util import f64, oracle_weights, rowwise_rel_err
-from gpu_common import GATE_ATOL, TOL_BF16, dev, np_f32, np_i, say
+from gpu_common import GATE_ATOL, TOL_BF16, check_untapped, dev, np_f32, np_i, say
 
 pytestmark = pytest.mark.gpu
 
@@ -148,6 +148,7 @@ def _check_forward_dropless(w, seed, d):
     assert rowwise_rel_err(f64(taps["y_latent"]), ref["y_latent"]) <= TOL_BF16
     err = rowwise_rel_err(f64(y), ref["y"])
     assert err <= TOL_BF16, err
+    check_untapped(rcd.forward_dropless, cfg, weights, inp["x"], y)
     return y
 
 

@@ -14,7 +14,7 @@ import oracle
 import routing_capacity_dispatch_amd as rcd
 import synth
 from _util import f64, rowwise_rel_err
-from gpu_common import GATE_ATOL, bank_valid, dev, np_f32, np_i, say, tol
+from gpu_common import GATE_ATOL, bank_valid, check_untapped, dev, np_f32, np_i, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,7 @@ def test_forward_full_size_sampled(name, n_tok, n_exp):
     weights = {k: v for k, v in inp.items() if k != "x"}
     cfg = rcd.config_of(w)
     y, counts, taps = rcd.forward(cfg, weights, inp["x"], taps=True)
+    check_untapped(rcd.forward, cfg, weights, inp["x"], y)
     torch.cuda.synchronize()
     say("oracle", name)
     rng = np.random.default_rng(0)

@@ -11,7 +11,7 @@ import oracle
 import routing_capacity_dispatch_amd as rcd
 import synth
 from _util import f64, oracle_weights, rowwise_rel_err
-from gpu_common import GATE_ATOL, bank_valid, dev, np_f32, np_i, say, tol
+from gpu_common import GATE_ATOL, bank_valid, check_untapped, dev, np_f32, np_i, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -296,7 +296,9 @@ def _check_forward(w, seed, d, **over):
     assert rowwise_rel_err(f64(taps["y_latent"]), ref["y_latent"]) <= t
     err = rowwise_rel_err(f64(y), ref["y"])
     assert err <= t, err
+    check_untapped(rcd.forward, cfg, weights, inp["x"], y)
     return y, ref
+
 
 
 @pytest.mark.parametrize("name,seed", FORWARD_CASES)
