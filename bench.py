@@ -45,7 +45,7 @@ STAGE_KERNEL = {
     "expert_gate_up": ("ragged_gemm_kernel", ">, 1>("),
     "expert_down": ("ragged_gemm_kernel", ">, 0>("),
     "shared_gate_up": ("swiglu_bf16_kernel",),
-    "output": ("dense_bf16_kernel",),
+    "output": ("densecat_bf16_kernel",),
     "combine": ("combine_kernel",),
     "scatter": ("scatter_kernel",),
     "swiglu_bwd": ("ragged_gemm_kernel", ">, 2>("),
@@ -191,6 +191,19 @@ def cpu_baseline_bias(logits, top_k, n_bins):
                       f"{n} oracle calls of {dt:.2f} s (numpy, single-threaded)"}
 
 
+def blas_info():
+    """Threads and vendor of the BLAS numpy calls (threadpoolctl), or (0, None)."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # threadpoolctl missing: report the affinity mask
+        return 0, None
+    if not libs:
+        return 0, None
+    best = max(libs, key=lambda i: i.get("num_threads", 0))
+    return best.get("num_threads", 0), f"{best.get('internal_api')} {best.get('version')}"
+
+
 def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
     """The fp64 oracle on the first n_tok tokens (its own batch: caps are
     derived for n_tok tokens), weights given as the run's bf16 values."""
@@ -198,12 +211,7 @@ def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
     import torch
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 0) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [0])
-    except Exception:  # threadpoolctl missing: report the affinity mask
-        blas_threads = 0
+    blas_threads, blas = blas_info()
     cores = len(os.sched_getaffinity(0))
 
     def f64(t):
@@ -247,7 +255,7 @@ def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
         what = (f"first {n_tok} tokens of the {w.name} inputs as their own batch "
                 f"({'no caps' if dropless else f'caps for {n_tok} tokens'})")
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": blas_threads or cores,
-            "kind": "oracle",
+            "kind": "oracle", "blas": blas,
             "sample": f"{what}, fp64 numpy, {dt:.1f} s wall, {cores} cores in the affinity mask"}
 
 
@@ -481,22 +489,33 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # headline: the plain call, one event per step boundary (events on the
+    # stream the library launches on: torch's current stream)
+    tev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    for row in ev:       # torch creates its events lazily, on first record
-        for e in row:
-            e.record()
+    for e in tev + [e for row in ev for e in row]:   # torch creates its events lazily
+        e.record()
     print(f"# timing {K} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
+    tev[0].record()
     for i in range(K):
-        step.profiled(arg, ev[i])
-    t_end.record()
+        step(arg)
+        tev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / K
+    ms_step = tev[0].elapsed_time(tev[K]) / K
+    per_step = [tev[i].elapsed_time(tev[i + 1]) for i in range(K)]
+    # the median of steps 2 .. K-1 (1-based; 2-19 of 20), as the pages
+    # quote a run's step time
+    mid = sorted(per_step[1:K - 1] if K >= 4 else per_step)
+    ms_median = (mid[(len(mid) - 1) // 2] + mid[len(mid) // 2]) / 2
+
+    # stage breakdown: a second pass through the instrumented entry point
+    print(f"# stage pass, {K} steps", file=sys.stderr, flush=True)
+    for i in range(K):
+        step.profiled(arg, ev[i])
+    torch.cuda.synchronize()
 
     per = {s: 0.0 for s in stages}
     for i in range(K):
@@ -551,6 +570,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "median_ms_steps_2_19" if K == 20 else f"median_ms_steps_2_{K - 1}": round(ms_median, 4),
+        "median_tokens_per_s": round(w.T / (ms_median * 1e-3), 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -119,8 +119,9 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
                                       : capacity(c->send_cap_num, c->send_cap_den, Tw, k, P);
   const int64_t cr = c->cap_recv_rows ? c->cap_recv_rows
                                       : capacity(c->recv_cap_num, c->recv_cap_den, Tw, k, E);
-  // every index the kernels form stays inside int32
-  if (W * P * cs > kI32Max || W * E * cr > kI32Max || E * W * cr > kI32Max)
+  // every index the kernels form stays inside int32 (each capacity first, so
+  // no product can overflow: W, P, E < 2^17)
+  if (cs > kI32Max || cr > kI32Max || W * P * cs > kI32Max || W * E * cr > kI32Max)
     return MOE_ERR_UNSUPPORTED;
   const int64_t eb = c->dtype == MOE_BF16 ? 2 : 4;
   const int64_t L = c->d_latent, F = c->d_ff;

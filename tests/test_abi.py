@@ -316,3 +316,15 @@ def test_router_bias_update_validation(lib):
     assert prof(C.byref(cfg_ok), fake, 64, fake, nul, nul, fake, n.value, nul, nul, 5) == abi.MOE_ERR_INVALID_ARG
     ev = (C.c_void_p * 4)()
     assert prof(C.byref(cfg_ok), fake, 64, fake, nul, nul, fake, n.value, nul, ev, 4) == abi.MOE_ERR_INVALID_ARG
+
+
+def test_huge_explicit_caps_unsupported(lib):
+    # an explicit capacity beyond int32 is rejected before any product with
+    # W, P or E is formed (no int64 overflow on the way)
+    for field in ("cap_send_rows", "cap_recv_rows"):
+        cfg = rcd.config_of(synth.workload("mid_bf16"))
+        setattr(cfg, field, 1 << 60)
+        assert _status(lambda: rcd.plan(cfg)) == abi.MOE_ERR_UNSUPPORTED
+        setattr(cfg, field, (1 << 31))
+        assert _status(lambda: rcd.plan(cfg)) == abi.MOE_ERR_UNSUPPORTED
+
