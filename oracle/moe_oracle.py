@@ -405,12 +405,17 @@ def forward_dropless(x, w, *, top_k, routing_logits32=None, tokens=None):
 
 
 def bank_expert_rows(rows, bank_rows, expert_count, expert_weights, experts,
-                     pool=0, row_filter=None):
-    """SwiGLU_e of the bank rows binned to expert e, for e in `experts`.
+                     row_filter=None):
+    """SwiGLU_e of the bank rows binned to expert e, for e in `experts`: the
+    receiver side of one destination ([LJ §2]: the receiver cap bounds the
+    rows of one local expert; [RH §3.2]: each wave's receive buffer holds
+    the expected rows of that wave x 1.15).
 
-    rows [W, C_send, L] is one pool's block per wave; bank_rows[w, e, r] is
-    the pool slot of the r-th row of expert e.  Returns {(w, s): o}.
-    row_filter(w, s) -> bool restricts the computed rows.
+    rows[w][s] is the row in slot s of the destination's block of wave w;
+    bank_rows[w, e, r] is the pool slot of the r-th row wave w binned to
+    expert e, for r < expert_count[w, e] (later entries are not read).
+    Returns {(w, s): o}.  row_filter(w, s) -> bool restricts the computed
+    rows.
     """
     out = {}
     W = bank_rows.shape[0]

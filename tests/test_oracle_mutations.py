@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.moe_oracle as om
 import test_oracle_assign as ta
+import test_oracle_bank as tbk
 import test_oracle_capacity as tc
 import test_oracle_forward as tf
 import test_oracle_router as tr
@@ -315,3 +316,72 @@ def test_round_to_nearest_bin_is_caught(monkeypatch):
         return np.minimum(np.rint(p).astype(np.int64), n_bins - 1)
     monkeypatch.setattr(rbm, "bin_index", nearest)
     assert _some_bias_pin_fails()
+
+
+# ------------------------------------------------------------------ receiver side
+def _bank_variant(pick):
+    """bank_expert_rows with the (w, r) -> (row wave, slot) map replaced."""
+    def bad(rows, bank_rows, expert_count, expert_weights, experts, row_filter=None):
+        out = {}
+        W, _, C = bank_rows.shape
+        for e in experts:
+            wg, wu, wd = expert_weights(int(e))
+            sel = [x for w in range(W) for x in pick(bank_rows, expert_count, w, int(e), C)]
+            sel = [(w, s) for (w, s) in sel if row_filter is None or row_filter(w, s)]
+            if not sel:
+                continue
+            o = om.swiglu(np.stack([np.asarray(rows[w][s], np.float64) for w, s in sel]), wg, wu, wd)
+            out.update({ws: v for ws, v in zip(sel, o)})
+        return out
+    return bad
+
+
+def test_bank_rows_pins_pass_on_the_real_oracle():
+    tbk.test_bank_rows_equal_forward_expert_outputs()
+    tbk.test_bank_rows_single_wave_by_hand()
+
+
+def test_bank_rows_swapped_waves_are_caught(monkeypatch):
+    # the row lists of wave w read against the pool block of another wave
+    pick = lambda br, ec, w, e, C: [(w, int(br[(w + 1) % br.shape[0], e, r]))
+                                    for r in range(int(ec[(w + 1) % br.shape[0], e]))]
+    monkeypatch.setattr(oracle, "bank_expert_rows", _bank_variant(pick))
+    assert _fails(tbk.test_bank_rows_equal_forward_expert_outputs)
+
+
+def test_bank_rows_read_past_count_are_caught(monkeypatch):
+    # every entry of the row list, not just the first expert_count
+    pick = lambda br, ec, w, e, C: [(w, int(br[w, e, r])) for r in range(C)]
+    monkeypatch.setattr(oracle, "bank_expert_rows", _bank_variant(pick))
+    assert _fails(tbk.test_bank_rows_equal_forward_expert_outputs)
+
+
+def test_bank_rows_off_by_one_slot_is_caught(monkeypatch):
+    pick = lambda br, ec, w, e, C: [(w, int(br[w, e, r]) + 1) for r in range(int(ec[w, e]))]
+    monkeypatch.setattr(oracle, "bank_expert_rows", _bank_variant(pick))
+    assert _fails(tbk.test_bank_rows_single_wave_by_hand)
+
+
+def test_bank_rows_receiver_slot_as_pool_slot_is_caught(monkeypatch):
+    # the receiver slot r taken as the pool slot (no bank_rows lookup)
+    pick = lambda br, ec, w, e, C: [(w, r) for r in range(int(ec[w, e]))]
+    monkeypatch.setattr(oracle, "bank_expert_rows", _bank_variant(pick))
+    assert _fails(tbk.test_bank_rows_equal_forward_expert_outputs)
+
+
+def test_drop_fractions_swapped_ends_are_caught(monkeypatch):
+    def bad(a, T, k):
+        n = T * k
+        return dict(sender=a["receiver_dropped"] / n, receiver=a["sender_dropped"] / n,
+                    total=(a["sender_dropped"] + a["receiver_dropped"]) / n)
+    monkeypatch.setattr(oracle, "drop_fractions", bad)
+    assert _fails(tbk.test_drop_fractions_hand_count)
+    assert _fails(tbk.test_drop_fractions_conservation)
+
+
+def test_drop_fractions_per_token_denominator_is_caught(monkeypatch):
+    def bad(a, T, k):
+        sd, rd = a["sender_dropped"], a["receiver_dropped"]
+        return dict(sender=sd / T, receiver=rd / T, total=(sd + rd) / T)
+    monkeypatch.setattr(oracle, "drop_fractions", bad)
+    assert _fails(tbk.test_drop_fractions_hand_count)
