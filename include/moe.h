@@ -261,6 +261,28 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx,
                         int64_t* counts, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* moe_dispatch for callers that cannot allocate device memory: code under
+   HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+   The same work and the same results as moe_dispatch, with its scratch (the
+   dispatch_ws_bytes moe_dispatch takes as ws) in a library-owned device
+   array of moe_dispatch_noalloc_scratch_bytes() = 4 MiB instead of a
+   workspace argument; the call allocates nothing.  Each GPU the library
+   runs on holds its own copy of the array until the process ends.  Every
+   call on one GPU shares that GPU's copy: calls that overlap on one GPU (on
+   different streams, or from different host threads) race and must be
+   serialised by the caller.  All other arguments as in moe_dispatch.
+   Errors: as moe_dispatch; MOE_ERR_WORKSPACE when the shape's
+   dispatch_ws_bytes exceeds the array; MOE_ERR_HIP when the array's device
+   address cannot be obtained. */
+moe_status moe_dispatch_noalloc(const moe_config* cfg, const int32_t* topk_idx,
+                                const void* z, void* pools, int32_t* pool_slot,
+                                int32_t* recv_slot, int32_t* bank_rows,
+                                int32_t* pool_count, int32_t* expert_count,
+                                int64_t* counts, void* stream);
+
+/* Bytes of moe_dispatch_noalloc's scratch array (per GPU). */
+int64_t moe_dispatch_noalloc_scratch_bytes(void);
+
 /* Routed experts over the received pool blocks (ranhao.site section 2.2:
    384 routed experts of width 3072; SwiGLU, no biases).  For every expert e,
    the rows of all waves binned to it form one group:

@@ -159,6 +159,20 @@ def dispatch(cfg, topk_idx: torch.Tensor, z: torch.Tensor) -> Dict[str, torch.Te
     return out
 
 
+def dispatch_noalloc(cfg, topk_idx: torch.Tensor, z: torch.Tensor, out: Dict[str, torch.Tensor]):
+    """moe_dispatch_noalloc into caller-provided outputs (the dict that
+    dispatch() returns, or one shaped like it); allocates nothing."""
+    abi.check("moe_dispatch_noalloc", library().moe_dispatch_noalloc(
+        C.byref(cfg), _ptr(topk_idx), _ptr(z), _ptr(out["pools"]), _ptr(out["pool_slot"]),
+        _ptr(out["recv_slot"]), _ptr(out["bank_rows"]), _ptr(out["pool_count"]),
+        _ptr(out["expert_count"]), _ptr(out["counts"]), _stream(z.device)))
+    return out
+
+
+def dispatch_noalloc_scratch_bytes() -> int:
+    return library().moe_dispatch_noalloc_scratch_bytes()
+
+
 def pool_views(cfg, pools: torch.Tensor):
     """(rows [W, P, C_send, L], ids [W, P, C_send]) views of a pools buffer."""
     p = plan(cfg)

@@ -77,6 +77,8 @@ SIGNATURES = {
                                                   C.c_size_t, _P, _P, C.c_int32]),
     "moe_dispatch": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, C.c_size_t, _P]),
+    "moe_dispatch_noalloc": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_noalloc_scratch_bytes": (C.c_int64, []),
     "moe_experts": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P,
                               C.c_size_t, _P]),
     "moe_combine": (C.c_int, [C.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P]),

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -537,6 +539,62 @@ MOE_API moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, 
   if (!ws || (int64_t)ws_bytes < p.dispatch_ws_bytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
   return run_dispatch(cfg, p, topk_idx, z, pools, pool_slot, recv_slot, bank_rows, pool_count,
                       expert_count, counts, ws, static_cast<hipStream_t>(stream), nullptr);
+}
+
+// ---- dispatch without allocation -----------------------------------------
+// The scratch of moe_dispatch_noalloc (per-wave counters and per-chunk key
+// counts, the same bytes moe_dispatch takes as its workspace) lives in this
+// file-scope device array: every GPU the library runs on holds one copy at
+// its own address until the process ends.  In host code the array's name is
+// a host-side stand-in, never a device address: only the pointer that
+// hipGetSymbolAddress returns for the current device is handed to kernels.
+namespace {
+
+constexpr int64_t kNoallocScratchBytes = int64_t(4) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char noalloc_scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the array, looked up once per device (with
+// that device current) on the first call that runs there.
+moe_status noalloc_scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API int64_t moe_dispatch_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+MOE_API moe_status moe_dispatch_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* z,
+                                        void* pools, int32_t* pool_slot, int32_t* recv_slot,
+                                        int32_t* bank_rows, int32_t* pool_count, int32_t* expert_count,
+                                        int64_t* counts, void* stream) {
+  moe_plan p;
+  moe_status st = plan_impl(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!pool_count || !expert_count || !counts) return MOE_ERR_INVALID_ARG;
+  if ((p.pools_bytes > 0 && !pools) || (p.cap_recv > 0 && !bank_rows)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!topk_idx || !z || !pool_slot || !recv_slot)) return MOE_ERR_INVALID_ARG;
+  if (p.dispatch_ws_bytes > kNoallocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  st = noalloc_scratch_ptr(&scratch);
+  if (st != MOE_OK) return st;
+  // the kernels clear what they accumulate into (the first workgroup of the
+  // count pass zeroes the per-wave counters; every chunk count that is read
+  // is written first), so the array's previous contents do not matter
+  return run_dispatch(cfg, p, topk_idx, z, pools, pool_slot, recv_slot, bank_rows, pool_count,
+                      expert_count, counts, scratch, static_cast<hipStream_t>(stream), nullptr);
 }
 
 MOE_API moe_status moe_experts(const moe_config* cfg, const void* pools, const int32_t* bank_rows,

@@ -328,3 +328,20 @@ def test_huge_explicit_caps_unsupported(lib):
         setattr(cfg, field, (1 << 31))
         assert _status(lambda: rcd.plan(cfg)) == abi.MOE_ERR_UNSUPPORTED
 
+
+
+def test_dispatch_noalloc_validation(lib):
+    # host checks come before the scratch's device address is looked up
+    nul = None
+    fake = C.c_void_p(0x100000)
+    assert lib.moe_dispatch_noalloc_scratch_bytes() == 4 << 20
+    cfg = rcd.config_of(synth.workload("mid_bf16"))
+    assert lib.moe_dispatch_noalloc(C.byref(cfg), fake, fake, fake, fake, fake, fake, fake, fake,
+                                    nul, nul) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_noalloc(C.byref(cfg), nul, fake, fake, fake, fake, fake, fake, fake,
+                                    fake, nul) == abi.MOE_ERR_INVALID_ARG
+    # a shape whose scratch exceeds the array: 1M tokens x 8 over 1024 experts
+    big = rcd.make_config(1 << 20, 64, 64, 1024, 1024, 8, 64, n_waves=1, dtype="bf16")
+    assert rcd.plan(big)["dispatch_ws_bytes"] > lib.moe_dispatch_noalloc_scratch_bytes()
+    assert lib.moe_dispatch_noalloc(C.byref(big), fake, fake, fake, fake, fake, fake, fake, fake,
+                                    fake, nul) == abi.MOE_ERR_WORKSPACE
