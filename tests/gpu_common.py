@@ -54,3 +54,51 @@ def check_untapped(fwd, cfg, weights, x, y_tapped):
     if a.dtype == torch.bfloat16:
         a, b = a.view(torch.int16), b.view(torch.int16)
     assert torch.equal(a, b)
+
+
+def check_weight_grads(dw, ref_dw, rows, t):
+    """Weight gradients of every expert against the oracle (reading B7): an
+    expert that kept no row must get exact zeros; every other expert's
+    gradient matrix must be within t in max-norm (max |diff| / max |ref|);
+    experts with at least 32 rows must also be within t row by row.
+    dw: the three [E, out, in] gradients in the order the backward returns
+    them; ref_dw[e]: the oracle's three for expert e in the same order, fp64.
+    Returns the worst max-norm and row-wise errors."""
+    from _util import f64, rowwise_rel_err
+    worst_mx, worst_rw = 0.0, 0.0
+    for e in range(len(rows)):
+        for i in range(3):
+            if rows[e] == 0:
+                assert torch.count_nonzero(dw[i][e]) == 0, (e, i)
+                continue
+            g, r = f64(dw[i][e]), ref_dw[e][i]
+            mx = float(np.abs(g - r).max() / np.abs(r).max())
+            assert mx <= t, ("max-norm", e, i, int(rows[e]), mx)
+            worst_mx = max(worst_mx, mx)
+            if rows[e] >= 32:
+                rw = rowwise_rel_err(g, r)
+                assert rw <= t, ("row-wise", e, i, int(rows[e]), rw)
+                worst_rw = max(worst_rw, rw)
+    return worst_mx, worst_rw
+
+
+def check_logits(logits32, z, w_router, ref_logits, ref_z, t):
+    """Router logits (reading R21): against the router GEMM of the path's own
+    z (fp64 over the same stored operands) within 1e-5 of each element's
+    magnitude bound sum_l |z_l| |W_el|; against the fp64 oracle row by row
+    within t when a row holds at least 8 experts, and within t of that
+    magnitude bound for every element (rows of 4 experts included)."""
+    from _util import rowwise_rel_err
+    lg = np.asarray(logits32, dtype=np.float64)
+    own = z @ w_router.T
+    bound = np.abs(z) @ np.abs(w_router).T
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = np.where(bound > 0, np.abs(lg - own) / np.where(bound > 0, bound, 1.0), np.abs(lg - own))
+    assert float(q.max(initial=0.0)) <= 1e-5, ("logits vs own z", float(q.max()))
+    bref = np.abs(ref_z) @ np.abs(w_router).T
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = np.where(bref > 0, np.abs(lg - ref_logits) / np.where(bref > 0, bref, 1.0), np.abs(lg - ref_logits))
+    assert float(q.max(initial=0.0)) <= t, ("logits vs oracle, element bound", float(q.max()))
+    if lg.shape[1] >= 8:
+        err = rowwise_rel_err(lg, ref_logits)
+        assert err <= t, ("logits vs oracle, row-wise", err)

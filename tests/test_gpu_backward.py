@@ -17,7 +17,7 @@ import oracle
 import routing_capacity_dispatch_amd as rcd
 import synth
 from _util import f64, oracle_weights, rowwise_rel_err
-from gpu_common import dev, np_f32, np_i, say, tol
+from gpu_common import check_weight_grads, dev, np_f32, np_i, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -80,11 +80,7 @@ def _check_all(w, seed, d):
     sel = np.zeros((w.T, w.n_experts), dtype=bool)
     np.put_along_axis(sel, topk, True, axis=1)
     assert np.all(np_f32(d_logits)[~sel] == 0)
-    for i, name in enumerate(("dw_gate", "dw_up", "dw_down")):
-        got = f64(dw[i])
-        want = np.stack([ref["dw"][e][i] for e in range(w.n_experts)])
-        err = rowwise_rel_err(got.reshape(-1, got.shape[-1]), want.reshape(-1, want.shape[-1]))
-        assert err <= t, (name, err)
+    check_weight_grads(dw, ref["dw"], np_i(fwd.tap_t["expert_count"]).sum(axis=0), t)
     return cfg, inp, fwd, bwd, dy, ref
 
 
@@ -106,13 +102,14 @@ def test_backward_routed_special_cases(over):
     _check_all(w, 3, d)
 
 
-def test_backward_with_empty_experts_and_ragged_tokens():
+@pytest.mark.parametrize("seed", [5, 6, 7, 8, 9, 10])
+def test_backward_with_empty_experts_and_ragged_tokens(seed):
     # 77 tokens, top-1 over 64 experts: most experts get no row, and their
-    # weight gradients must be written as zeros
+    # weight gradients must be written as zeros; the others keep 1-4 rows
     d = dev()
-    say("backward empty experts")
+    say("backward empty experts", seed)
     w = synth.workload("mid_bf16", T=77, top_k=1)
-    cfg, inp, fwd, bwd, dy, ref = _check_all(w, 5, d)
+    cfg, inp, fwd, bwd, dy, ref = _check_all(w, seed, d)
     ec = np_i(fwd.tap_t["expert_count"]).sum(axis=0)
     assert (ec == 0).any()
     for e in np.nonzero(ec == 0)[0]:
@@ -256,10 +253,7 @@ def test_backward_dropless_mid(seed):
     t = tol(w.dtype)
     assert rowwise_rel_err(f64(dz), ref["dz"]) <= t
     assert rowwise_rel_err(np_f32(d_logits).astype(np.float64), ref["d_logits"]) <= t
-    for i in range(3):
-        got = f64(dw[i])
-        want = np.stack([ref["dw"][e][i] for e in range(w.n_experts)])
-        assert rowwise_rel_err(got.reshape(-1, got.shape[-1]), want.reshape(-1, want.shape[-1])) <= t, i
+    check_weight_grads(dw, ref["dw"], np.bincount(topk.ravel(), minlength=w.n_experts), t)
 
 
 def test_backward_dropless_components_compose_bitwise():

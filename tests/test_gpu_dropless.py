@@ -12,7 +12,7 @@ import oracle
 import routing_capacity_dispatch_amd as rcd
 import synth
 from _util import f64, oracle_weights, rowwise_rel_err
-from gpu_common import GATE_ATOL, TOL_BF16, check_untapped, dev, np_f32, np_i, say
+from gpu_common import GATE_ATOL, TOL_BF16, check_logits, check_untapped, dev, np_f32, np_i, say
 
 pytestmark = pytest.mark.gpu
 
@@ -145,6 +145,7 @@ def _check_forward_dropless(w, seed, d):
     assert np.array_equal(np_i(taps["expert_offsets"]), ref["offsets"])
     assert np_i(counts).tolist() == [w.T * w.top_k, 0, 0]
     assert rowwise_rel_err(f64(taps["z"]), ref["z"]) <= TOL_BF16
+    check_logits(logits32, f64(taps["z"]), f64(inp["w_router"]), ref["logits"], ref["z"], TOL_BF16)
     assert rowwise_rel_err(f64(taps["y_latent"]), ref["y_latent"]) <= TOL_BF16
     err = rowwise_rel_err(f64(y), ref["y"])
     assert err <= TOL_BF16, err

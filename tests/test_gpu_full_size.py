@@ -3,8 +3,11 @@ benchmark times (one moe_forward call).
 
 Integer results (top-k, slots, counts, id columns, receiver lists) are
 compared in full against the oracle's assignment from the same fp32 logits.
-Values are compared on samples the fp64 oracle computes one by one: sampled
-tokens' z, logits and y, and every kept row of sampled experts.
+Values are compared on samples the fp64 oracle computes one by one: 64+
+sampled tokens' z, logits and y (including tokens routed to the sampled
+experts), and every kept row of sampled experts: one expert per M-tile count
+at the Marin shape, the most loaded experts (multi-band tile order) at the
+Zipf-skewed one.
 """
 import numpy as np
 import pytest
@@ -26,18 +29,31 @@ def _dense_weights(inp):
     return out
 
 
-def _expert_fn(inp):
-    cache = {}
-
-    def ew(e):
-        if e not in cache:
-            cache[e] = (f64(inp["w_gate"][e]), f64(inp["w_up"][e]), f64(inp["w_down"][e]))
-        return cache[e]
-    return ew
+def _expert_fn_uncached(inp):
+    """Expert weights in fp64, converted on each call (the oracle asks for
+    each expert once per call, and hundreds of experts would not fit)."""
+    return lambda e: (f64(inp["w_gate"][e]), f64(inp["w_up"][e]), f64(inp["w_down"][e]))
 
 
-@pytest.mark.parametrize("name,n_tok,n_exp", [("marin_16k", 8, 3), ("zipf_64k", 6, 2)])
-def test_forward_full_size_sampled(name, n_tok, n_exp):
+GEMM_TILE_ROWS = 192  # M tile of the routed grouped GEMMs
+
+
+def _checked_experts(name, rows, rng):
+    """Experts whose every kept row is checked.  Zipf-skewed workload: the
+    three most loaded (up to 9 M tiles: two bands of the tile order, the
+    longest K loops' worth of tiles) and one other; otherwise one expert for
+    each M-tile count present."""
+    present = np.nonzero(rows > 0)[0]
+    if name.startswith("zipf"):
+        top = [int(e) for e in np.argsort(-rows, kind="stable")[:3]]
+        rest = np.setdiff1d(present, top)
+        return top + [int(rng.choice(rest))]
+    tiles = -(-rows // GEMM_TILE_ROWS)
+    return [int(rng.choice(np.nonzero(tiles == m)[0])) for m in np.unique(tiles[present])]
+
+
+@pytest.mark.parametrize("name", ["marin_16k", "zipf_64k"])
+def test_forward_full_size_sampled(name):
     d = dev()
     w = synth.workload(name)
     say("full-size forward", name)
@@ -49,9 +65,21 @@ def test_forward_full_size_sampled(name, n_tok, n_exp):
     torch.cuda.synchronize()
     say("oracle", name)
     rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(w.T, n_tok, replace=False))
+    # sampled experts (chosen from the GPU's receiver counts, which are
+    # checked against the oracle in full below) and 64+ sampled tokens:
+    # 64 at random and 4 routed to (and kept by) each sampled expert
+    kept_rows = np_i(taps["expert_count"]).sum(axis=0)
+    experts = _checked_experts(name, kept_rows, rng)
+    say("checked experts", name, [(e, int(kept_rows[e])) for e in experts])
+    gtopk, grecv = np_i(taps["topk_idx"]), np_i(taps["recv_slot"])
+    pick = set(rng.choice(w.T, 64, replace=False).tolist())
+    for e in experts:
+        cand = np.unique(np.nonzero((gtopk == e) & (grecv >= 0))[0])
+        pick.update(rng.choice(cand, min(4, len(cand)), replace=False).tolist())
+    toks = np.array(sorted(pick))
+    assert len(toks) >= 64
     wt = _dense_weights(inp)
-    wt["expert_weights"] = _expert_fn(inp)
+    wt["expert_weights"] = _expert_fn_uncached(inp)
     logits32 = np_f32(taps["logits"])
     ref = oracle.forward(np_f32(inp["x"]), wt, top_k=w.top_k, n_pools=w.n_pools,
                          n_waves=w.n_waves, routing_logits32=logits32, tokens=toks)
@@ -84,12 +112,11 @@ def test_forward_full_size_sampled(name, n_tok, n_exp):
     Tw = -(-w.T // w.n_waves)
     epp = w.n_experts // w.n_pools
     topk = ref["topk_idx"]
-    for e in rng.choice(w.n_experts, n_exp, replace=False):
+    for e in experts:
         ti, ji = np.nonzero((topk == e) & (a["recv_slot"] >= 0))
-        if not len(ti):
-            continue
+        assert len(ti) == kept_rows[e]
         zr = f64(taps["z"][torch.from_numpy(ti).to(d)])
-        o = oracle.swiglu(zr, *_expert_fn(inp)(int(e)))
+        o = oracle.swiglu(zr, *_expert_fn_uncached(inp)(int(e)))
         got = view[torch.from_numpy(ti // Tw).to(d), int(e) // epp,
                    torch.from_numpy(a["pool_slot"][ti, ji]).to(d)]
         assert rowwise_rel_err(f64(got), o) <= t
@@ -123,7 +150,7 @@ def test_recv_share_sampled():
     torch.cuda.synchronize()
     say("oracle recv share")
     rng = np.random.default_rng(1)
-    toks = np.sort(rng.choice(T, 16, replace=False))
+    toks = np.sort(rng.choice(T, 64, replace=False))
     Tw = sh["Tw"]
     need = {}
     for t in toks:

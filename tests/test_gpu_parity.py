@@ -11,7 +11,7 @@ import oracle
 import routing_capacity_dispatch_amd as rcd
 import synth
 from _util import f64, oracle_weights, rowwise_rel_err
-from gpu_common import GATE_ATOL, bank_valid, check_untapped, dev, np_f32, np_i, say, tol
+from gpu_common import GATE_ATOL, bank_valid, check_logits, check_untapped, dev, np_f32, np_i, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -282,7 +282,7 @@ def _check_forward(w, seed, d, **over):
                          routing_logits32=logits32)
     t = tol(w.dtype)
     assert rowwise_rel_err(f64(taps["z"]), ref["z"]) <= t
-    assert rowwise_rel_err(logits32.astype(np.float64), ref["logits"]) <= t
+    check_logits(logits32, f64(taps["z"]), wt["w_router"], ref["logits"], ref["z"], t)
     assert np.array_equal(np_i(taps["topk_idx"]), ref["topk_idx"])
     assert np.abs(np_f32(taps["gates"]) - ref["gates"]).max() <= GATE_ATOL
     a = ref["assignment"]

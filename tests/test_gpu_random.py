@@ -2,16 +2,19 @@
 
 Forward (capped and dropless), the routed-path backward (capped and
 dropless) and the router bias update over random token counts, expert and
-pool counts, top-k, wave counts, widths, shared experts and capacity factors
-(including a zero factor), with the same bars as the fixed cases: indices,
-slots, counts and histograms bit-exact, values within the row-wise tolerance.
+pool counts (4 experts included), top-k, wave counts, widths, shared experts
+and capacity factors (including a zero factor), with the same bars as the
+fixed cases: indices, slots, counts and histograms bit-exact, values within
+the row-wise tolerance.
 
-Two kinds of row make the row-wise metric ill-conditioned and are left out:
-logit rows of only 4 experts (their max-norm can be small next to the bf16
-rounding of z), and weight-gradient rows of experts that kept fewer than 32
-rows (each such row is a short sum of rank-one terms whose size can rest on a
-few cancelling values); for those experts the backward is checked for exact
-zeros when the expert kept nothing.
+Two kinds of value are compared with the condition-aware bars of readings
+R21 and B7 (the row-wise bar measures their conditioning, not the kernels):
+router logits in rows of fewer than 8 experts (each element within the
+tolerance of its magnitude bound sum_l |z_l| |W_el|, and the router GEMM of
+the path's own z within 1e-5 of it), and the weight gradients of experts
+that kept 1 to 31 rows (each expert's gradient matrix within the tolerance
+in max-norm; experts with no row get exact zeros).  The row-wise bar on
+those gradients is kept as an expected failure that records the class.
 """
 import random
 
@@ -22,7 +25,7 @@ import torch
 import oracle
 import synth
 from _util import f64, oracle_weights, rowwise_rel_err
-from gpu_common import dev, np_f32, np_i, say, tol
+from gpu_common import check_weight_grads, dev, np_f32, np_i, say, tol
 import test_gpu_backward as gb
 import test_gpu_bias as gbias
 import test_gpu_dropless as gd
@@ -82,12 +85,27 @@ def _check_backward(w, seed, dropless):
     t = tol(w.dtype)
     assert rowwise_rel_err(f64(dz), ref["dz"]) <= t
     assert rowwise_rel_err(np_f32(d_logits).astype(np.float64), ref["d_logits"]) <= t
-    for e in range(w.n_experts):
-        for i in range(3):
-            if rows[e] >= 32:
-                assert rowwise_rel_err(f64(dw[i][e]), ref["dw"][e][i]) <= t, (e, i)
-            elif rows[e] == 0:
-                assert torch.count_nonzero(dw[i][e]) == 0, (e, i)
+    check_weight_grads(dw, ref["dw"], rows, t)
+    return dw, ref, rows
+
+
+def _four_experts(i):
+    rng = random.Random(3000 + i)
+    return synth.Workload(f"random_e4_{i}", T=rng.choice([1, 63, 300, 1500, 2500]), d_model=64 * rng.randint(1, 4),
+                          d_latent=256 * rng.randint(1, 2), n_experts=4, n_pools=rng.choice([1, 2, 4]),
+                          top_k=rng.randint(1, 4), d_ff=256, n_shared=rng.randint(0, 2), d_ff_shared=128,
+                          n_waves=rng.randint(1, 3), dtype=rng.choice(["bf16", "bf16", "f32"]), bias="normal",
+                          bias_std=rng.choice([0.0, 0.01]), send_cap=rng.choice([(11, 10), (1, 2)]),
+                          recv_cap=rng.choice([(23, 20), (1, 3)]))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_forward_random_four_experts(i):
+    w = _four_experts(i)
+    say("random forward, 4 experts", w)
+    gp._check_forward(w, 600 + i, dev())
+    if w.dtype == "bf16":
+        gd._check_forward_dropless(w, 700 + i, dev())
 
 
 @pytest.mark.parametrize("i", range(N_CASES // 2))
@@ -96,6 +114,23 @@ def test_backward_random(i):
     say("random backward", w)
     _check_backward(w, 300 + i, dropless=False)
     _check_backward(w, 400 + i, dropless=True)
+
+
+@pytest.mark.xfail(strict=False, reason=(
+    "row-wise weight gradients of experts with 1-31 rows: a row is a short sum of rank-one terms "
+    "whose size can rest on cancelling dh values and on silu'(a) near its zero, so its relative "
+    "error is the elementwise error of da / db (do and dh are stored bf16, reading B5); reading B7 "
+    "compares these experts in max-norm instead"))
+def test_backward_rowwise_small_experts():
+    worst = 0.0
+    for i in range(4):
+        w = _shape(50 + i, backward=True)
+        say("random backward, row-wise on small experts", w)
+        dw, ref, rows = _check_backward(w, 300 + i, dropless=False)
+        for e in np.nonzero((rows > 0) & (rows < 32))[0]:
+            for m in range(3):
+                worst = max(worst, rowwise_rel_err(f64(dw[m][e]), ref["dw"][e][m]))
+    assert worst <= tol("bf16"), worst
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
