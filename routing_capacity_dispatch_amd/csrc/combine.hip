@@ -21,16 +21,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // lane j < k: the pool row and gate of the token's assignment j, all
   // loaded at once (an assignment whose expert id or pool slot is out of
   // range adds nothing)
-  int64_t row = -1;
-  float g = 0.0f;
-  if (lane < k) {
-    const int64_t q = t * k + lane;
-    const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
-    if (rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send) {
-      row = (w * a.P + e / epp) * a.cap_send + ps;
-      g = a.gates ? a.gates[q] : 1.0f;
-    }
-  }
+  // (every lane loads: lanes past k re-read the last assignment, so no
+  // branch separates the loads)
+  const int64_t q = t * k + min(lane, k - 1);
+  const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
+  const float gq = a.gates ? a.gates[q] : 1.0f;
+  const bool ok = lane < k && rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send;
+  const int64_t row = ok ? (w * a.P + e / epp) * a.cap_send + ps : -1;
+  const float g = ok ? gq : 0.0f;
   combine_rows<T>(a.expert_out, row, g, k, a.row_bytes,
                   static_cast<char*>(a.y) + t * (a.y_pitch ? a.y_pitch : a.row_bytes));
 }

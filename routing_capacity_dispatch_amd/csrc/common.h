@@ -57,6 +57,11 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Streaming store of data the next kernel reads once (nontemporal hint)
+__device__ __forceinline__ void st16_stream(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Unpack a 16-byte chunk of T into floats: 4 (f32) or 8 (bf16) values.
 __device__ __forceinline__ void unpack(const uint4& v, float* out, float) {
   out[0] = __uint_as_float(v.x);
@@ -113,6 +118,13 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits, uint64_t a
   return m;
 }
 
+// Lane `l`'s 64-bit value (l wave-uniform), read into scalar registers.
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint64_t>(v)), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint64_t>(v) >> 32), l);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Lane `src`'s 64-bit value, broadcast to the wavefront.
 __device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
   const uint32_t lo = __shfl(static_cast<uint32_t>(v), src);
@@ -125,6 +137,11 @@ __device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
 // order, stored as T.  Rows are row_bytes (a multiple of 16) apart from
 // base.  Two rows' loads are in flight per step.  Each row is read once, so
 // the reads carry the nontemporal hint.
+// Every load is unconditional (a branch between loads makes the compiler
+// wait for all earlier loads before the next): a dropped assignment reads
+// one of the token's kept rows with weight 0 (adding +-0 leaves every sum
+// unchanged, and kept rows are finite), and chunk indices past the row's end
+// are clamped and not stored.  A token with no kept row gets zeros.
 template <typename T>
 __device__ __forceinline__ void combine_rows(const char* __restrict__ base, int64_t row, float g, int k,
                                              int64_t row_bytes, char* __restrict__ dst) {
@@ -132,6 +149,14 @@ __device__ __forceinline__ void combine_rows(const char* __restrict__ base, int6
   constexpr int CPL = 6;  // 16-byte chunks per lane per pass: a 3072-wide bf16 row in one pass
   const int lane = threadIdx.x & 63;
   const int chunks = (int)(row_bytes / 16);
+  const uint64_t kept = ballot64(lane < k && row >= 0);
+  if (kept == 0) {
+    for (int c = lane; c < chunks; c += 64) st16(dst + (int64_t)c * 16, make_uint4(0, 0, 0, 0));
+    return;
+  }
+  const int64_t stand_in = shfl64(row, __builtin_ctzll(kept));
+  const int64_t r_l = (lane < k && row >= 0) ? row : stand_in;
+  const float g_l = (lane < k && row >= 0) ? g : 0.0f;
   for (int seg = 0; seg < chunks; seg += 64 * CPL) {
     float acc[CPL][EPC];
 #pragma unroll
@@ -139,31 +164,28 @@ __device__ __forceinline__ void combine_rows(const char* __restrict__ base, int6
 #pragma unroll
       for (int q = 0; q < EPC; ++q) acc[i][q] = 0.0f;
     for (int j = 0; j < k; j += 2) {
-      const int64_t r0 = shfl64(row, j);
-      const int64_t r1 = j + 1 < k ? shfl64(row, j + 1) : -1;
-      const float g0 = __shfl(g, j), g1 = __shfl(g, j + 1);
+      // the two rows' addresses and gates are wave-uniform: scalar registers
+      const int j1 = j + 1 < k ? j + 1 : j;
+      const char* p0 = base + readlane64(r_l, j) * row_bytes;
+      const char* p1 = base + readlane64(r_l, j1) * row_bytes;
+      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g_l), j));
+      const float g1 = j + 1 < k ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g_l), j1)) : 0.0f;
       uint4 v0[CPL], v1[CPL];
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const int c = seg + i * 64 + lane;
-        if (c < chunks && r0 >= 0) v0[i] = ld16_stream(base + r0 * row_bytes + (int64_t)c * 16);
-        if (c < chunks && r1 >= 0) v1[i] = ld16_stream(base + r1 * row_bytes + (int64_t)c * 16);
+        const uint32_t c = (uint32_t)min(seg + i * 64 + lane, chunks - 1) * 16u;
+        v0[i] = ld16_stream(p0 + c);
+        v1[i] = ld16_stream(p1 + c);
       }
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const int c = seg + i * 64 + lane;
-        if (c >= chunks) continue;
         float f[EPC];
-        if (r0 >= 0) {
-          unpack(v0[i], f, T{});
+        unpack(v0[i], f, T{});
 #pragma unroll
-          for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g0, f[q], acc[i][q]);
-        }
-        if (r1 >= 0) {
-          unpack(v1[i], f, T{});
+        for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g0, f[q], acc[i][q]);
+        unpack(v1[i], f, T{});
 #pragma unroll
-          for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g1, f[q], acc[i][q]);
-        }
+        for (int q = 0; q < EPC; ++q) acc[i][q] = fmaf(g1, f[q], acc[i][q]);
       }
     }
 #pragma unroll

@@ -109,15 +109,21 @@ __device__ __forceinline__ int swiglu_feature(int r, int& half) {
 }
 
 // Write staged rows out in 16-byte chunks: row r of the tile goes to
-// row_ptr(r) (already at the tile's first column).
-template <class TL, class RowPtr>
+// row_ptr(r) (already at the tile's first column).  kStream: nontemporal
+// stores, for outputs the next kernel streams once (no reuse from cache).
+template <class TL, bool kStream = false, class RowPtr>
 __device__ __forceinline__ void copy_rows(const char* lds, int ld, int chunks_per_row, int valid_rows,
                                           int valid_chunks, RowPtr row_ptr) {
   const int total = TL::BM * chunks_per_row;
   for (int q = threadIdx.x; q < total; q += TL::THREADS) {
     const int r = q / chunks_per_row;
     const int c = q - r * chunks_per_row;
-    if (r < valid_rows && c < valid_chunks) st16(row_ptr(r) + c * 16, ld16(lds + r * ld + c * 16));
+    if (r < valid_rows && c < valid_chunks) {
+      if constexpr (kStream)
+        st16_stream(row_ptr(r) + c * 16, ld16(lds + r * ld + c * 16));
+      else
+        st16(row_ptr(r) + c * 16, ld16(lds + r * ld + c * 16));
+    }
   }
 }
 
@@ -489,7 +495,8 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
   __syncthreads();
   const int cpr = tile_cols * 2 / 16;
   const int32_t* ci = p.c_index;
-  copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0), min(cpr, (cols - c0) * 2 / 16), [&](int r) {
+  // the down-projection's rows are read once, by the combine
+  copy_rows<TL, !kSwiglu>(lds, ld, cpr, min(TL::BM, rows - m0), min(cpr, (cols - c0) * 2 / 16), [&](int r) {
     const int64_t row = ci ? ci[row0 + m0 + r] : row0 + m0 + r;
     return p.C + row * p.c_row_bytes + (int64_t)c0 * 2;
   });

@@ -248,12 +248,12 @@ __global__ __launch_bounds__(256) void ragged_combine_kernel(const char* __restr
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  int64_t row = -1;
-  float g = 0.0f;
-  if (lane < k) {
-    row = row_of[t * k + lane];
-    if (row >= 0) g = gates ? gates[t * k + lane] : 1.0f;
-  }
+  // (every lane loads: lanes past k re-read the last assignment)
+  const int64_t q = t * k + min(lane, k - 1);
+  const int64_t r = row_of[q];
+  const float gq = gates ? gates[q] : 1.0f;
+  const int64_t row = lane < k ? r : -1;
+  const float g = lane < k && r >= 0 ? gq : 0.0f;
   combine_rows<T>(out, row, g, k, row_bytes, y + t * y_pitch);
 }
 
