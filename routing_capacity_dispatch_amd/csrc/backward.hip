@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 // d_gates = 0 and no row.  Lanes j < k load the token's assignments at once;
 // the o rows are then read two at a time.  dy and o are read once, so their
 // loads carry the nontemporal hint.
-template <int kMaxChunks>
+template <int kMaxChunks, bool kRowOf>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -136,72 +136,79 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   const int k = a.k, epp = a.E / a.P;
   const int64_t w = t / a.Tw;
   const int chunks = (int)(a.row_bytes / 16);
-  int64_t row = -1;
-  float g = 0.0f;
-  if (lane < k) {
-    const int64_t q = t * k + lane;
-    if (a.row_of) {  // dropless: the assignment's row in expert order
-      row = a.row_of[q];
-    } else {
-      const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
-      if (rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send) row = (w * a.P + e / epp) * a.cap_send + ps;
-    }
-    if (row >= 0) g = a.gates[q];
+  // No branch separates the loads of a step (a branch between loads makes
+  // the compiler wait for every earlier load before the next): every lane
+  // loads an assignment (lanes past k re-read the last one), chunk indices
+  // past the row's end are clamped (their products are not used), and a
+  // dropped assignment reads one of the token's kept rows (its dot product
+  // is not used and it stores nothing).
+  const int64_t q = t * k + min(lane, k - 1);
+  int64_t row;
+  if constexpr (kRowOf) {  // dropless: the assignment's row in expert order
+    row = a.row_of[q];
+  } else {
+    const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
+    // (& rather than &&: no short-circuit branch to sink a load into)
+    row = (rs >= 0) & (e >= 0) & (e < a.E) & (ps >= 0) & (ps < a.cap_send) ? (w * a.P + e / epp) * a.cap_send + ps : -1;
   }
+  const float gq = a.gates[q];
+  if (lane >= k) row = -1;
+  const float g = row >= 0 ? gq : 0.0f;
   // dy[t] in registers: chunk c = i * 64 + lane
   float dy[kMaxChunks][8];
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = i * 64 + lane;
-    if (c < chunks)
-      unpack(ld16_stream(static_cast<const char*>(a.dy) + t * a.row_bytes + (int64_t)c * 16), dy[i], bf16_t{});
-  }
+  for (int i = 0; i < kMaxChunks; ++i)
+    unpack(ld16_stream(static_cast<const char*>(a.dy) + t * a.row_bytes + (int64_t)min(i * 64 + lane, chunks - 1) * 16),
+           dy[i], bf16_t{});
   float dg = 0.0f;  // lane j < k ends with d_gates[t, j]
-  for (int j = 0; j < k; j += 2) {
-    const int64_t r0 = shfl64(row, j);
-    const int64_t r1 = j + 1 < k ? shfl64(row, j + 1) : -1;
-    const float g0 = __shfl(g, j), g1 = __shfl(g, j + 1);
-    uint4 v0[kMaxChunks], v1[kMaxChunks];
-    const char* o0 = static_cast<const char*>(a.expert_out) + r0 * a.row_bytes;
-    const char* o1 = static_cast<const char*>(a.expert_out) + r1 * a.row_bytes;
+  const uint64_t kept = ballot64(row >= 0);
+  if (kept) {
+    const int64_t r_l = row >= 0 ? row : shfl64(row, __builtin_ctzll(kept));
+    for (int j = 0; j < k; j += 2) {
+      const int j1 = j + 1 < k ? j + 1 : j;
+      const bool k0 = readlane64(row, j) >= 0;
+      const bool k1 = j + 1 < k && readlane64(row, j1) >= 0;
+      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), j));
+      const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), j1));
+      const int64_t rb0 = readlane64(r_l, j) * a.row_bytes, rb1 = readlane64(r_l, j1) * a.row_bytes;
+      const char* o0 = static_cast<const char*>(a.expert_out) + rb0;
+      const char* o1 = static_cast<const char*>(a.expert_out) + rb1;
+      uint4 v0[kMaxChunks], v1[kMaxChunks];
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
-      const int c = i * 64 + lane;
-      if (c < chunks && r0 >= 0) v0[i] = ld16_stream(o0 + (int64_t)c * 16);
-      if (c < chunks && r1 >= 0) v1[i] = ld16_stream(o1 + (int64_t)c * 16);
-    }
-    float s0 = 0.0f, s1 = 0.0f;
+      for (int i = 0; i < kMaxChunks; ++i) {
+        const uint32_t c = (uint32_t)min(i * 64 + lane, chunks - 1) * 16u;
+        v0[i] = ld16_stream(o0 + c);
+        v1[i] = ld16_stream(o1 + c);
+      }
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
-      const int c = i * 64 + lane;
-      if (c >= chunks) continue;
-      float f[8], out[8];
-      if (r0 >= 0) {
+      for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = i * 64 + lane;
+        if (c >= chunks) continue;
+        float f[8], out[8];
         unpack(v0[i], f, bf16_t{});
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           s0 = fmaf(dy[i][x], f[x], s0);
           out[x] = g0 * dy[i][x];
         }
-        st16(static_cast<char*>(a.d_expert_out) + r0 * a.row_bytes + (int64_t)c * 16, pack(out, bf16_t{}));
-      }
-      if (r1 >= 0) {
+        if (k0) st16(static_cast<char*>(a.d_expert_out) + rb0 + (int64_t)c * 16, pack(out, bf16_t{}));
         unpack(v1[i], f, bf16_t{});
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           s1 = fmaf(dy[i][x], f[x], s1);
           out[x] = g1 * dy[i][x];
         }
-        st16(static_cast<char*>(a.d_expert_out) + r1 * a.row_bytes + (int64_t)c * 16, pack(out, bf16_t{}));
+        if (k1) st16(static_cast<char*>(a.d_expert_out) + rb1 + (int64_t)c * 16, pack(out, bf16_t{}));
       }
-    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      s0 += __shfl_xor(s0, m);
-      s1 += __shfl_xor(s1, m);
+      for (int m = 32; m >= 1; m >>= 1) {
+        s0 += __shfl_xor(s0, m);
+        s1 += __shfl_xor(s1, m);
+      }
+      if (lane == j) dg = k0 ? s0 : 0.0f;
+      if (lane == j + 1) dg = k1 ? s1 : 0.0f;
     }
-    if (lane == j) dg = r0 >= 0 ? s0 : 0.0f;
-    if (lane == j + 1) dg = r1 >= 0 ? s1 : 0.0f;
   }
   if (lane < k) a.d_gates[t * k + lane] = dg;
 }
@@ -277,12 +284,13 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((a.T + 3) / 4);
   const int64_t chunks = a.row_bytes / 16;
+  const bool ro = a.row_of != nullptr;
   if (chunks <= 64 * 2)
-    combine_bwd_kernel<2><<<blocks, 256, 0, s>>>(a);
+    ro ? combine_bwd_kernel<2, true><<<blocks, 256, 0, s>>>(a) : combine_bwd_kernel<2, false><<<blocks, 256, 0, s>>>(a);
   else if (chunks <= 64 * 6)
-    combine_bwd_kernel<6><<<blocks, 256, 0, s>>>(a);
+    ro ? combine_bwd_kernel<6, true><<<blocks, 256, 0, s>>>(a) : combine_bwd_kernel<6, false><<<blocks, 256, 0, s>>>(a);
   else if (chunks <= 64 * 16)
-    combine_bwd_kernel<16><<<blocks, 256, 0, s>>>(a);
+    ro ? combine_bwd_kernel<16, true><<<blocks, 256, 0, s>>>(a) : combine_bwd_kernel<16, false><<<blocks, 256, 0, s>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t q = t * k + min(lane, k - 1);
   const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
   const float gq = a.gates ? a.gates[q] : 1.0f;
-  const bool ok = lane < k && rs >= 0 && e >= 0 && e < a.E && ps >= 0 && ps < a.cap_send;
+  // (& rather than &&: no short-circuit branch to sink a load into)
+  const bool ok = (lane < k) & (rs >= 0) & (e >= 0) & (e < a.E) & (ps >= 0) & (ps < a.cap_send);
   const int64_t row = ok ? (w * a.P + e / epp) * a.cap_send + ps : -1;
   const float g = ok ? gq : 0.0f;
   combine_rows<T>(a.expert_out, row, g, k, a.row_bytes,

@@ -84,15 +84,23 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float* __restrict
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + t * E;
+  // every lane loads every slot (past E: the last expert again, unused), so
+  // no branch separates the loads and they are all in flight together
+  float v[NPER], b[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) v[i] = row[min(i * 64 + lane, E - 1)];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) b[i] = 0.0f;
+  if (bias) {
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) b[i] = bias[min(i * 64 + lane, E - 1)];
+  }
   uint32_t key[NPER];
 #pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int e = i * 64 + lane;
-    key[i] = 0;
+  for (int i = 0; i < NPER; ++i)
     // at least 1 (only one NaN pattern maps to 0), so with k <= E every
     // round finds a present expert
-    if (e < E) key[i] = max(score_key(row[e] + (bias ? bias[e] : 0.0f)), 1u);
-  }
+    key[i] = i * 64 + lane < E ? max(score_key(v[i] + b[i]), 1u) : 0u;
   int mine = -1;  // lane j < k ends with the j-th selected expert
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0;
