@@ -40,7 +40,7 @@ using ExpertTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;
 // are four N tiles, so the Marin-shaped router GEMM is 512 tiles, two per CU
 using RouterTile = core::Tile<128, 96, 2, 2, 64, 2>;
 
-constexpr int kGroupM = 8;  // M panels per group of the dense tile order
+constexpr int kGroupM = 4;  // M panels per group of the dense tile order (4: measured best of 2, 4, 6, 8, 16)
 constexpr int kStagePad = 16;
 
 template <class TL>
