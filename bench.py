@@ -204,7 +204,7 @@ def blas_info():
     return best.get("num_threads", 0), f"{best.get('internal_api')} {best.get('version')}"
 
 
-def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
+def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None, min_seconds=0.0):
     """The fp64 oracle on the first n_tok tokens (its own batch: caps are
     derived for n_tok tokens), weights given as the run's bf16 values."""
     import numpy as np
@@ -244,19 +244,86 @@ def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None):
                 f"gradients, computed and discarded) of the first {n_tok} tokens of the {w.name} "
                 f"inputs as their own batch ({'no caps' if dropless else f'caps for {n_tok} tokens'})")
     else:
+        # calls repeated until min_seconds of work (one call by default)
         t0 = time.perf_counter()
-        if dropless:
-            r = oracle.forward_dropless(x, wt, top_k=w.top_k)
-        else:
-            r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
-                               send_cap=w.send_cap, recv_cap=w.recv_cap)
-        dt = time.perf_counter() - t0
+        calls = 0
+        while True:
+            if dropless:
+                r = oracle.forward_dropless(x, wt, top_k=w.top_k)
+            else:
+                r = oracle.forward(x, wt, top_k=w.top_k, n_pools=w.n_pools, n_waves=w.n_waves,
+                                   send_cap=w.send_cap, recv_cap=w.recv_cap)
+            calls += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        dt = (time.perf_counter() - t0) / calls
         assert r["y"].shape == (n_tok, w.d_model)
         what = (f"first {n_tok} tokens of the {w.name} inputs as their own batch "
-                f"({'no caps' if dropless else f'caps for {n_tok} tokens'})")
+                f"({'no caps' if dropless else f'caps for {n_tok} tokens'})"
+                + (f", {calls} calls" if calls > 1 else ""))
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": blas_threads or cores,
             "kind": "oracle", "blas": blas,
             "sample": f"{what}, fp64 numpy, {dt:.1f} s wall, {cores} cores in the affinity mask"}
+
+
+def cpu_baseline_recv_share(sh, n_tok, dev):
+    """The fp64 oracle on the first n_tok tokens of a receive share: their k
+    bank rows each through the owning expert's SwiGLU, then the combine."""
+    import numpy as np
+    import torch
+
+    import oracle
+    k = sh["k"]
+    ex = sh["expert_of"][:n_tok].numpy()
+    sl = sh["slot_of"][:n_tok].numpy()
+    wv = np.repeat((np.arange(n_tok) // sh["Tw"])[:, None], k, axis=1)
+    u = sh["rows"][torch.from_numpy(wv).to(dev).long(), torch.from_numpy(sl).to(dev).long()]
+    u = u.to("cpu", torch.float32).numpy().astype(np.float64)          # [n_tok, k, L]
+    ws = {int(e): tuple(sh[n][int(e)].to("cpu", torch.float32).numpy().astype(np.float64)
+                        for n in ("w_gate", "w_up", "w_down")) for e in np.unique(ex)}
+    g64 = sh["gates"][:n_tok].numpy().astype(np.float64)
+    t_c = time.perf_counter()
+    o = np.zeros((n_tok, k, u.shape[-1]))
+    for e in np.unique(ex):
+        m = ex == e
+        o[m] = oracle.swiglu(u[m], *ws[int(e)])
+    oracle.combine(g64, np.zeros((n_tok, k)), o)
+    dt = time.perf_counter() - t_c
+    cores = len(os.sched_getaffinity(0))
+    threads, blas = blas_info()
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads or cores, "kind": "oracle", "blas": blas,
+            "sample": f"the first {n_tok} tokens' {k} rows each through their experts' SwiGLU "
+                      f"and the combine, fp64 numpy, {dt:.1f} s wall, {cores} cores in the affinity mask"}
+
+
+# the oracle timed once per workload (context for the GPU figures; bounded samples)
+CPU_CONFIGS = [("tiny_fp32", 256), ("mid_bf16", 512), ("marin_16k", 256), ("recv_share", 16384),
+               ("zipf_64k", 256)]
+
+
+def cpu_baselines_by_config(main_name, main_result, seed, dev):
+    """One oracle timing per workload on a bounded token sample of it (the
+    headline workload's is main_result)."""
+    import torch
+
+    import synth
+    out = []
+    for name, n_tok in CPU_CONFIGS:
+        print(f"# cpu baseline: {name}, {n_tok} tokens", file=sys.stderr, flush=True)
+        if name == main_name and main_result is not None:
+            r = main_result
+        elif name == "recv_share":
+            sh = synth.make_recv_share(seed=seed, device=dev)
+            r = cpu_baseline_recv_share(sh, n_tok, dev)
+            del sh
+        else:
+            w = synth.workload(name)
+            inp = synth.make_inputs(w, seed, device=dev)
+            r = cpu_baseline(w, inp, n_tok, min_seconds=2.0)
+            del inp
+        torch.cuda.empty_cache()
+        out.append(dict(r, workload=name))
+    return out
 
 
 METRIC_SHARE = "MoE receive-share (6 local experts) SwiGLU + combine tokens/sec on 1 MI355X; % bf16 MFMA peak"
@@ -357,27 +424,7 @@ def bench_recv_share(args):
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or 32768
         print(f"# cpu baseline: oracle on the first {n_tok} tokens", file=sys.stderr, flush=True)
-        import oracle
-        ex = sh["expert_of"][:n_tok].numpy()
-        sl = sh["slot_of"][:n_tok].numpy()
-        wv = np.repeat((np.arange(n_tok) // sh["Tw"])[:, None], k, axis=1)
-        u = sh["rows"][torch.from_numpy(wv).to(dev).long(), torch.from_numpy(sl).to(dev).long()]
-        u = u.to("cpu", torch.float32).numpy().astype(np.float64)          # [n_tok, k, L]
-        ws = {int(e): tuple(sh[n][int(e)].to("cpu", torch.float32).numpy().astype(np.float64)
-                            for n in ("w_gate", "w_up", "w_down")) for e in np.unique(ex)}
-        g64 = sh["gates"][:n_tok].numpy().astype(np.float64)
-        t_c = time.perf_counter()
-        o = np.zeros((n_tok, k, L))
-        for e in np.unique(ex):
-            m = ex == e
-            o[m] = oracle.swiglu(u[m], *ws[int(e)])
-        oracle.combine(g64, np.zeros((n_tok, k)), o)
-        dt = time.perf_counter() - t_c
-        out["cpu_baseline"] = {"value": n_tok / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
-                               "kind": "oracle",
-                               "sample": f"the first {n_tok} tokens' {k} rows each through their experts' SwiGLU "
-                                         f"and the combine, fp64 numpy, {dt:.1f} s wall, "
-                                         f"{len(os.sched_getaffinity(0))} cores in the affinity mask"}
+        out["cpu_baseline"] = cpu_baseline_recv_share(sh, n_tok, dev)
     print(json.dumps(out), flush=True)
 
 
@@ -402,6 +449,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="oracle sample for the CPU baseline (default 256; 64 with --backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-configs", action="store_true",
+                    help="time the oracle on the headline workload only, not once per workload")
     ap.add_argument("--traffic", default=None,
                     help="measured HBM bytes per launch of the dominant kernel (JSON; default "
                          "profiles/traffic_<workload>.json)")
@@ -598,6 +647,9 @@ def main():
         print(f"# cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, dropless=args.dropless,
                                            backward=args.backward, dy_latent=dy)
+        if pass_name == "forward" and not args.dropless and not args.no_cpu_configs:
+            del fwd, step, inp, weights, x
+            out["cpu_baseline_configs"] = cpu_baselines_by_config(w.name, out["cpu_baseline"], args.seed, dev)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
