@@ -204,10 +204,8 @@ __device__ __forceinline__ void scatter_row(const char* __restrict__ src, char* 
   for (int seg = 0; seg < chunks; seg += 64 * 8) {
     uint4 r[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = seg + i * 64 + lane;
-      if (c < chunks) r[i] = ld16(src + (int64_t)c * 16);
-    }
+    for (int i = 0; i < 8; ++i)  // clamped past the row's end (not stored): no branch between the loads
+      r[i] = ld16(src + (int64_t)min(seg + i * 64 + lane, chunks - 1) * 16);
     for (int j = 0; j < k; ++j) {
       char* d = reinterpret_cast<char*>(shfl64(reinterpret_cast<int64_t>(dst), j));
       if (!d) continue;

@@ -200,15 +200,33 @@ __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a, const char
   if (t >= a.T) return;
   const int k = a.k, epp = a.E / a.P;
   const int64_t w = t / a.Tw;
-  char* dst = nullptr;
-  if (lane < k) {
-    const int ps = a.pool_slot[t * k + lane];
-    if (ps >= 0) {
-      const int p = a.topk[t * k + lane] / epp;
-      dst = a.pools + (w * a.P + p) * a.block_bytes + (int64_t)ps * a.row_bytes;
+  const char* src = z + t * a.row_bytes;
+  const int chunks = (int)(a.row_bytes / 16);
+  // a row of up to 512 chunks: its loads first (clamped past the row's end,
+  // not stored), then the assignments' (every lane loads: lanes past k
+  // re-read the last one), so no branch separates any of the loads
+  uint4 r[8];
+  if (chunks <= 512) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = ld16(src + (int64_t)min(i * 64 + lane, chunks - 1) * 16);
+  }
+  const int64_t q = t * k + min(lane, k - 1);
+  const int ps = a.pool_slot[q], e = a.topk[q];
+  const int64_t off = (w * a.P + e / epp) * a.block_bytes + (int64_t)ps * a.row_bytes;  // used only if kept
+  char* dst = (lane < k) & (ps >= 0) ? a.pools + off : nullptr;
+  if (chunks > 512) {
+    scatter_row(src, dst, k, a.row_bytes);
+    return;
+  }
+  for (int j = 0; j < k; ++j) {
+    char* d = reinterpret_cast<char*>(readlane64(reinterpret_cast<int64_t>(dst), j));
+    if (!d) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i * 64 + lane;
+      if (c < chunks) st16(d + (int64_t)c * 16, r[i]);
     }
   }
-  scatter_row(z + t * a.row_bytes, dst, k, a.row_bytes);
 }
 
 // Receiver side: one wavefront per (wave, pool) block reads only the id
