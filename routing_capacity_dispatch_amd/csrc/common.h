@@ -20,12 +20,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (inputs are finite)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (lo in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32.  On every finite input it equals adding 0x7FFF plus
+// the lowest kept bit to the fp32 bit pattern and keeping the high half
+// (checked over all finite fp32 patterns on the device).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// fp32 -> bf16, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return static_cast<uint16_t>(bf16_pair(f, 0.0f)); }
 
 template <typename T>
 struct ElemOps;
@@ -85,8 +92,7 @@ __device__ __forceinline__ uint4 pack(const float* in, bf16_t) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    w[i] = static_cast<uint32_t>(f32_to_bf16(in[2 * i])) |
-           (static_cast<uint32_t>(f32_to_bf16(in[2 * i + 1])) << 16);
+    w[i] = bf16_pair(in[2 * i], in[2 * i + 1]);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 

@@ -459,7 +459,7 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
             h = sa * b;
           }
           *reinterpret_cast<uint16_t*>(lds + row * ld + col * 2) = f32_to_bf16(da);
-          acc.v[mi][2 * q][r] = __uint_as_float((uint32_t)f32_to_bf16(db) | ((uint32_t)f32_to_bf16(h) << 16));
+          acc.v[mi][2 * q][r] = __uint_as_float(bf16_pair(db, h));
         }
     __syncthreads();
     char* DA = p.C + (int64_t)(row0 + m0) * p.c_row_bytes + (int64_t)c0 * 2;

@@ -15,10 +15,10 @@
 //
 // dgrad tiles are 192 rows x 256 columns (8 wavefronts, 96 x 64 each, a
 // third LDS stage for the streaming weights) over device-built tile lists
-// like the forward's; wgrad tiles are 256 x 256 (8 wavefronts, 64 x 128
-// each), an expert's tiles dealt to one XCD.  dgrad runs the forward core's
-// split-barrier schedule with a K-major B operand; wgrad, with two K-major
-// operands, the plain two-stage one (gemm_core.h).
+// like the forward's, on the forward core's split-barrier schedule with a
+// K-major B operand (gemm_core.h).  wgrad tiles are 256 x 256 (8
+// wavefronts, 64 x 128 each), an expert's tiles dealt to one XCD, in a
+// persistent kernel of its own with both operands K-major (below).
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -27,6 +27,7 @@ namespace moe {
 namespace {
 
 using core::Acc;
+using core::Frags;
 using core::acc_col;
 using core::acc_row;
 using core::kload_col;
@@ -38,7 +39,7 @@ using core::RowSrc;
 using core::uniform_ptr;
 
 using DgradTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;  // the weights stream: a third B stage
-using WgradTile = core::Tile<256, 256, 4, 2, 64, 2, 2>;
+using WgradTile = core::Tile<256, 256, 4, 2, 32, 4>;
 constexpr int kStagePad = 16;
 
 template <class TL>
@@ -48,14 +49,20 @@ constexpr int lds_bytes() {
 
 __device__ __forceinline__ int xcd_order(int bid, int nblocks) { return (bid & 7) * (nblocks >> 3) + (bid >> 3); }
 
-template <class TL, class RowPtr>
+// kStream: nontemporal stores (outputs no later tile of the kernel reads)
+template <class TL, bool kStream = false, class RowPtr>
 __device__ __forceinline__ void copy_rows(const char* lds, int ld, int chunks_per_row, int valid_rows,
                                           RowPtr row_ptr) {
   const int total = TL::BM * chunks_per_row;
   for (int q = threadIdx.x; q < total; q += TL::THREADS) {
     const int r = q / chunks_per_row;
     const int c = q - r * chunks_per_row;
-    if (r < valid_rows) st16(row_ptr(r) + c * 16, ld16(lds + r * ld + c * 16));
+    if (r < valid_rows) {
+      if constexpr (kStream)
+        st16_stream(row_ptr(r) + c * 16, ld16(lds + r * ld + c * 16));
+      else
+        st16(row_ptr(r) + c * 16, ld16(lds + r * ld + c * 16));
+    }
   }
 }
 
@@ -135,43 +142,246 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
 }
 
 // ------------------------------------------------------------------ wgrad
-__global__ __launch_bounds__(WgradTile::THREADS) void wgrad_kernel(BwdWgrad p) {
+// Persistent: a workgroup walks every nx-th tile of its XCD's contiguous
+// share of the expert-major tile list (nx workgroups per XCD; an expert's
+// tiles output-row tile fastest, so the window of tiles running on one XCD
+// shares the expert's X columns) through one K pipeline that runs across
+// tile boundaries, so the loads of the next tile's first K tiles are in
+// flight while the current tile finishes and writes its output.  K tiles of
+// 32 in four stages, on a mid-tile barrier schedule split along N (below).
+//
+// The operands are swapped (the MFMA's M side is Y, the output's columns),
+// so each lane holds 4 consecutive output columns of a row; the output goes
+// out through a per-wavefront LDS area beside the stages, 16 rows at a
+// time, as whole 128-byte row segments with nontemporal stores (no later
+// tile of the kernel reads them).
+constexpr int kEpiPitch = 144;                      // bytes per staged output row (128 + 16)
+constexpr int kEpiWave = 16 * kEpiPitch;            // one wavefront's staging area
+constexpr int kEpiStores = WgradTile::WM * WgradTile::WN * 2 / 1024;  // store instructions per wavefront per tile
+
+// Wait until the loads of a K tile have landed when `after` K tiles were
+// issued after it and, if `stores`, at least one tile's output stores too
+// (memory operations of a wavefront complete in issue order), then
+// synchronise the workgroup.  The wavefront's LDS reads are complete first,
+// so a stage that every wavefront has read may be refilled after the
+// barrier.
+__device__ __forceinline__ void wgrad_wait(int after, bool stores) {
+  constexpr int P = WgradTile::A_INS + WgradTile::B_INS;
+  static_assert(WgradTile::NS == 4, "after is 0 .. 3");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (stores) {
+    if (after >= 3)
+      core::wait_loads<3 * P + kEpiStores>();
+    else if (after == 2)
+      core::wait_loads<2 * P + kEpiStores>();
+    else if (after == 1)
+      core::wait_loads<P + kEpiStores>();
+    else
+      core::wait_loads<kEpiStores>();
+  } else {
+    if (after >= 3)
+      core::wait_loads<3 * P>();
+    else if (after == 2)
+      core::wait_loads<2 * P>();
+    else if (after == 1)
+      core::wait_loads<P>();
+    else
+      core::wait_loads<0>();
+  }
+}
+
+// Fragments of one K tile split by N: all of A with the first half of B
+// (the first phase's MFMAs), and the second half of B.
+struct WgradHalf {
+  uint4 a[WgradTile::MI];
+  uint4 b[WgradTile::NI / 2];
+};
+
+template <int kFirst>
+__device__ __forceinline__ void wgrad_read_b(const char* sb, uint4* b, int wn, int lane) {
   using TL = WgradTile;
-  __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<TL>()];
+#pragma unroll
+  for (int j = 0; j < TL::NI / 2; ++j) b[j] = core::kfrag<TL::BN>(sb, wn * TL::WN + (kFirst + j) * 16, 0, lane);
+}
+
+__device__ __forceinline__ void wgrad_read_first(const char* sa, const char* sb, WgradHalf& h, int wm, int wn,
+                                                 int lane) {
+  using TL = WgradTile;
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i) h.a[i] = core::kfrag<TL::BM>(sa, wm * TL::WM + i * 16, 0, lane);
+  wgrad_read_b<0>(sb, h.b, wn, lane);
+}
+
+template <int kFirst>
+__device__ __forceinline__ void wgrad_mfma(const uint4* a, const uint4* b, Acc<WgradTile>& acc) {
+  using TL = WgradTile;
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::NI / 2; ++j)
+      acc.v[i][kFirst + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[j]), acc.v[i][kFirst + j], 0, 0, 0);
+}
+
+// nr LDS reads spread among nm MFMAs
+template <int nm, int nr>
+__device__ __forceinline__ void wgrad_interleave() {
+#pragma unroll
+  for (int i = 0; i < nr; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, nm / nr, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, nm - (nm / nr) * nr, 0);
+}
+
+// offsets: p.offsets as a separate restrict argument, so that the compiler
+// reads it with scalar loads (no store of the kernel can alias it) instead of
+// vector loads whose waits would drain the loads in flight
+__global__ __launch_bounds__(WgradTile::THREADS) void wgrad_kernel(BwdWgrad p,
+                                                                   const int32_t* __restrict__ offsets) {
+  using TL = WgradTile;
+  constexpr int NS = TL::NS;
+  constexpr int NM = TL::MI * TL::NI / 2;  // MFMAs per phase
+  __shared__ __attribute__((aligned(1024))) char lds[TL::MAIN_LDS + TL::NW * kEpiWave];
   const int per_e = p.tiles_m * p.tiles_n;
-  const int t = xcd_order(blockIdx.x, gridDim.x);
-  const int e = t / per_e;
-  if (e >= p.E) return;
-  const int r = t - e * per_e;
-  const int mt = r % p.tiles_m, nt = r / p.tiles_m;
-  const int m0 = mt * TL::BM, n0 = nt * TL::BN;
-  const int row0 = p.offsets[e];
-  const int ktiles = (p.offsets[e + 1] - row0) / 64;
+  const int total = p.E * per_e;
+  const int per_xcd = (total + 7) >> 3;
+  const int nx = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int t0 = xcd * per_xcd + (blockIdx.x >> 3);
+  const int t_end = min(total, (xcd + 1) * per_xcd);
+  if (t0 >= t_end) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  RowSrc<TL::A_INS> a_src;
-  RowSrc<TL::B_INS> b_src;
-  const char* A = uniform_ptr(p.X + (int64_t)row0 * p.x_row_bytes + p.x_col_bytes + (int64_t)m0 * 2);
-  const char* B = uniform_ptr(p.Y + (int64_t)row0 * p.y_row_bytes + p.y_col_bytes + (int64_t)n0 * 2);
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  char* lds_a = lds;
+  char* lds_b = lds + TL::B_BASE;
+  // per-lane offsets, the same in every tile: A = Y (K-major, BM wide),
+  // B = X (K-major, BN wide)
+  uint32_t a_off[TL::A_INS], b_off[TL::B_INS];
 #pragma unroll
   for (int i = 0; i < TL::A_INS; ++i) {
     const int kr = kload_row<TL, TL::BM>(i, wave, lane);
-    a_src.base[i] = A;
-    a_src.off[i] = (uint32_t)(kr * p.x_row_bytes) + kload_col<TL::BM>(kr, lane);
+    a_off[i] = (uint32_t)(kr * p.y_row_bytes) + kload_col<TL::BM>(kr, lane);
   }
 #pragma unroll
   for (int i = 0; i < TL::B_INS; ++i) {
     const int kr = kload_row<TL, TL::BN>(i, wave, lane);
-    b_src.base[i] = B;
-    b_src.off[i] = (uint32_t)(kr * p.y_row_bytes) + kload_col<TL::BN>(kr, lane);
+    b_off[i] = (uint32_t)(kr * p.x_row_bytes) + kload_col<TL::BN>(kr, lane);
+  }
+  const int64_t a_kstep = (int64_t)TL::BK * p.y_row_bytes, b_kstep = (int64_t)TL::BK * p.x_row_bytes;
+  // tile t: expert, output origin (m0 rows, n0 columns), K tiles (an even
+  // number: an expert's rows are padded to 64), and the wave-uniform bases
+  // of its Y and X columns
+  auto info = [&](int t, int& e, int& m0, int& n0, const char*& ya, const char*& xb) {
+    e = t / per_e;
+    const int r = t - e * per_e;
+    m0 = (r % p.tiles_m) * TL::BN;
+    n0 = (r / p.tiles_m) * TL::BM;
+    const int row0 = offsets[e];
+    ya = uniform_ptr(p.Y + (int64_t)row0 * p.y_row_bytes + p.y_col_bytes + (int64_t)n0 * 2);
+    xb = uniform_ptr(p.X + (int64_t)row0 * p.x_row_bytes + p.x_col_bytes + (int64_t)m0 * 2);
+    return (offsets[e + 1] - row0) / TL::BK;
+  };
+  // the load cursor: tile lt, K tile lk of its lkt
+  int lt = t0, lk = 0, lkt = 0;
+  const char* la = nullptr;
+  const char* lb = nullptr;
+  auto seek = [&]() {  // from lt on, the first tile with K tiles
+    for (; lt < t_end; lt += nx) {
+      int e, m0, n0;
+      lkt = info(lt, e, m0, n0, la, lb);
+      if (lkt > 0) break;
+    }
+  };
+  auto issue_next = [&](int stage) {
+    const int64_t ka = lk * a_kstep, kb = lk * b_kstep;
+#pragma unroll
+    for (int i = 0; i < TL::A_INS; ++i)
+      core::lds_load16(la + ka, a_off[i], lds_a + stage * TL::A_BYTES + (i * TL::NW + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < TL::B_INS; ++i)
+      core::lds_load16(lb + kb, b_off[i], lds_b + stage * TL::B_BYTES + (i * TL::NW + wave) * 1024);
+    if (++lk == lkt) {
+      lk = 0;
+      lt += nx;
+      seek();
+    }
+  };
+  // K tile s of this workgroup's sequence sits in stage s % NS; the loads
+  // of K tiles s + 1 .. s + NS are in flight while tile s is consumed:
+  //   phase 1: MFMAs of (s, A with B's first half) | reads of B's second half
+  //   phase 2: wait for tile s + 1, barrier (every read of tile s done)
+  //   phase 3: loads of tile s + NS into stage s % NS;
+  //            MFMAs of (s, B's second half) | reads of (s + 1, first half)
+  seek();
+  int issued = 0;  // K tiles issued so far
+  for (int j = 0; j < NS && lt < t_end; ++j) {
+    issue_next(j);
+    ++issued;
+  }
+  int s = 0;                // K tiles consumed so far
+  int last_epi = -4 * NS;   // the K tile after which the last output stores went out
+  char* ew = lds + TL::MAIN_LDS + wave * kEpiWave;
+  WgradHalf h0, h1;
+  uint4 b2[TL::NI / 2];
+  if (issued > 0) {
+    wgrad_wait(issued - 1, false);
+    wgrad_read_first(lds_a, lds_b, h0, wm, wn, lane);
   }
   Acc<TL> acc;
   acc.zero();
-  mainloop<TL, false, true, true>(a_src, b_src, ktiles, lds, acc, 64 * p.x_row_bytes, 64 * p.y_row_bytes);
-  constexpr int ld = TL::BN * 2 + kStagePad;
-  stage<TL>(acc, lds, ld, 0);
-  __syncthreads();
-  char* C = p.C + ((int64_t)e * p.M + m0) * p.N * 2 + (int64_t)n0 * 2;
-  copy_rows<TL>(lds, ld, TL::BN * 2 / 16, TL::BM, [&](int rr) { return C + (int64_t)rr * p.N * 2; });
+  // one K tile: the MFMAs on cur, the next tile's first half read into nxt
+  auto step = [&](WgradHalf& cur, WgradHalf& nxt) __attribute__((always_inline)) {
+    const int st = s % NS;
+    // phase 1
+    wgrad_read_b<TL::NI / 2>(lds_b + st * TL::B_BYTES, b2, wn, lane);
+    wgrad_mfma<0>(cur.a, cur.b, acc);
+    wgrad_interleave<NM, TL::NI>();
+    // phase 2: K tile s + 1 was issued before the loop or in iteration
+    // s + 1 - NS, ahead of that iteration's output stores
+    if (s + 1 < issued) wgrad_wait(issued - 1 - (s + 1), last_epi >= s + 1 - NS);
+    // phase 3 (the reads of a tile past the last one read a stale stage and
+    // go unused)
+    if (lt < t_end) {
+      issue_next(st);
+      ++issued;
+    }
+    const int st1 = (s + 1) % NS;
+    wgrad_read_first(lds_a + st1 * TL::A_BYTES, lds_b + st1 * TL::B_BYTES, nxt, wm, wn, lane);
+    wgrad_mfma<TL::NI / 2>(cur.a, b2, acc);
+    wgrad_interleave<NM, TL::MI * 2 + TL::NI>();
+    ++s;
+  };
+  for (int t = t0; t < t_end; t += nx) {
+    int e, m0, n0;
+    const char* ya;
+    const char* xb;
+    const int kt = info(t, e, m0, n0, ya, xb);
+    for (int k = 0; k < kt; k += 2) {
+      step(h0, h1);
+      step(h1, h0);
+    }
+    // output rows m0 + wn WN + ni 16 + (0..15), columns n0 + wm WM + (0..63):
+    // lane l holds row (l & 15) of block ni, columns mi 16 + 4 (l >> 4) + (0..3)
+    char* C = p.C + ((int64_t)e * p.M + m0 + wn * TL::WN) * p.N * 2 + (int64_t)(n0 + wm * TL::WM) * 2;
+#pragma unroll
+    for (int ni = 0; ni < TL::NI; ++ni) {
+#pragma unroll
+      for (int mi = 0; mi < TL::MI; ++mi) {
+        const f32x4_t v = acc.v[mi][ni];
+        const uint2 w = make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
+        *reinterpret_cast<uint2*>(ew + (lane & 15) * kEpiPitch + mi * 32 + (lane >> 4) * 8) = w;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = lane + 64 * h, row = q >> 3, c = q & 7;
+        st16_stream(C + (int64_t)(ni * 16 + row) * p.N * 2 + c * 16, ld16(ew + row * kEpiPitch + c * 16));
+      }
+    }
+    acc.zero();
+    last_epi = s - 1;
+  }
 }
 
 inline int pad8(int64_t n) { return (int)((n + 7) / 8 * 8); }
@@ -195,8 +405,16 @@ hipError_t launch_bwd_du(const BwdDgrad& p, int64_t max_entries, hipStream_t s) 
 }
 
 hipError_t launch_bwd_wgrad(const BwdWgrad& p, hipStream_t s) {
-  if (p.E <= 0) return hipSuccess;
-  wgrad_kernel<<<pad8((int64_t)p.E * p.tiles_m * p.tiles_n), WgradTile::THREADS, 0, s>>>(p);
+  const int64_t tiles = (int64_t)p.E * p.tiles_m * p.tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  // one persistent workgroup per CU (its LDS admits no second), a whole
+  // number per XCD
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t grid = std::min<int64_t>(pad8(tiles), std::max(8, cus / 8 * 8));
+  wgrad_kernel<<<(int)grid, WgradTile::THREADS, 0, s>>>(p, p.offsets);
   return hipGetLastError();
 }
 
