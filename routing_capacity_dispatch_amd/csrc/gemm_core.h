@@ -493,9 +493,13 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
                         lane);
       sb = sb1;
     }
+    // the last tile: its second half read after the first half's MFMAs,
+    // into the same registers (one fragment set live: with two, the
+    // accumulators of kernels at the register limit spill here)
     const int kl = ktiles - 1;
-    mfma_and_read<TL, AK, BK>(f0, acc, lds_a + (kl & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f1, wm, wn, lane);
-    mfma_frags<TL>(f1, acc);
+    mfma_frags<TL>(f0, acc);
+    read_frags<TL, AK, BK>(lds_a + (kl & 1) * TL::A_BYTES, lds_b + sb * TL::B_BYTES, 1, f0, wm, wn, lane);
+    mfma_frags<TL>(f0, acc);
   } else if constexpr ((AK || BK) && TL::NSB == TL::NS && TL::NS == 2 && TL::KS == 2) {
     // K-major operands on the plain schedule: the loads of tile kt + 1
     // after the barrier that frees its stage, then tile kt's MFMAs with the
