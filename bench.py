@@ -256,11 +256,15 @@ def cpu_baseline(w, inp, n_tok, dropless=False, backward=False, dy_latent=None, 
             calls += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
-        dt = (time.perf_counter() - t0) / calls
+        total = time.perf_counter() - t0
+        dt = total / calls
         assert r["y"].shape == (n_tok, w.d_model)
         what = (f"first {n_tok} tokens of the {w.name} inputs as their own batch "
-                f"({'no caps' if dropless else f'caps for {n_tok} tokens'})"
-                + (f", {calls} calls" if calls > 1 else ""))
+                f"({'no caps' if dropless else f'caps for {n_tok} tokens'})")
+        wall = f"{total:.1f} s wall over {calls} calls" if calls > 1 else f"{dt:.1f} s wall"
+        return {"value": n_tok / dt, "unit": "tokens/s", "cores": blas_threads or cores,
+                "kind": "oracle", "blas": blas,
+                "sample": f"{what}, fp64 numpy, {wall}, {cores} cores in the affinity mask"}
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": blas_threads or cores,
             "kind": "oracle", "blas": blas,
             "sample": f"{what}, fp64 numpy, {dt:.1f} s wall, {cores} cores in the affinity mask"}
