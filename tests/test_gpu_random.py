@@ -116,6 +116,23 @@ def test_backward_random(i):
     _check_backward(w, 400 + i, dropless=True)
 
 
+@pytest.mark.parametrize("dropless", [False, True])
+def test_backward_weight_grads_many_tiles_per_workgroup(dropless):
+    """More weight-gradient tiles than CUs (64 experts x 4 x 4 tiles of
+    256 x 256 at L = F = 1024), so each persistent workgroup walks several
+    tiles through one pipeline; a strongly biased router leaves some experts
+    empty and, in the dropless variant, gives others many times the mean row
+    count, so tiles of different K follow one another.  Every expert's gradients
+    against the oracle."""
+    w = synth.Workload("wgrad_many_tiles", T=1500, d_model=256, d_latent=1024, n_experts=64, n_pools=8,
+                       top_k=2, d_ff=1024, n_shared=0, d_ff_shared=128, n_waves=2, dtype="bf16",
+                       bias="normal", bias_std=2.0, send_cap=(11, 10), recv_cap=(23, 20))
+    say("backward, weight-gradient tiles beyond one per CU", w, "dropless" if dropless else "capped")
+    dw, ref, rows = _check_backward(w, 900 + int(dropless), dropless=dropless)
+    # (capped: the receiver cap keeps every expert below 64 rows)
+    assert (rows == 0).any() and (rows.max() > 64 or not dropless)
+
+
 @pytest.mark.xfail(strict=False, reason=(
     "row-wise weight gradients of experts with 1-31 rows: a row is a short sum of rank-one terms "
     "whose size can rest on cancelling dh values and on silu'(a) near its zero, so its relative "
