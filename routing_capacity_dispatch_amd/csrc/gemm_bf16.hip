@@ -411,6 +411,24 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
       b_src.off[i] = (uint32_t)(n * p.K * 2) + load_col<TL>(lane);
     }
   }
+  // the backward's dh tile: its loads go out before the K loop (into
+  // registers, landing in LDS after it), so their latency is not paid after
+  // the tile's last MFMA; zeros outside the expert's rows and features
+  constexpr int kDhChunks = kMode == 2 ? TL::BM * (TL::BN / 2) * 2 / 16 / TL::THREADS : 1;
+  uint4 dh_reg[kDhChunks];
+  if constexpr (kMode == 2) {
+    constexpr int cpr = (TL::BN / 2) * 2 / 16;
+    const int vr = min(TL::BM, rows - m0), vc = min(cpr, (p.F - c0) * 2 / 16);
+    const char* DH = p.dH + (int64_t)(row0 + m0) * p.dh_row_bytes + (int64_t)c0 * 2;
+#pragma unroll
+    for (int i = 0; i < kDhChunks; ++i) {
+      const int q = threadIdx.x + i * TL::THREADS;
+      const int r = q / cpr, c = q - r * cpr;
+      // clamped address, result selected: no branch between the loads
+      const uint4 v = ld16(DH + (int64_t)min(r, vr - 1) * p.dh_row_bytes + min(c, vc - 1) * 16);
+      dh_reg[i] = (r < vr) & (c < vc) ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
   Acc<TL> acc;
   acc.zero();
   mainloop<TL>(a_src, b_src, p.K / TL::BK, lds, acc);
@@ -427,17 +445,15 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
     constexpr int ld = (TL::BN / 2) * 2 + kStagePad;
     constexpr int cpr = (TL::BN / 2) * 2 / 16;
     const int vr = min(TL::BM, rows - m0), vc = min(cpr, (p.F - c0) * 2 / 16);
-    // the tile's dh rows, staged through LDS with coalesced 16-byte loads
-    // (zeros outside the expert's rows), after the staging area of the outputs
+    // the tile's dh rows (loaded before the K loop) staged through LDS,
+    // after the staging area of the outputs
+    static_assert(TL::BM * cpr == kDhChunks * TL::THREADS, "the dh tile is whole 16-byte chunks per thread");
     char* ldh = lds + ((TL::BM * ld + 1023) & ~1023);
-    {
-      const char* DH = p.dH + (int64_t)(row0 + m0) * p.dh_row_bytes + (int64_t)c0 * 2;
-      for (int q = threadIdx.x; q < TL::BM * cpr; q += TL::THREADS) {
-        const int r = q / cpr, c = q - r * cpr;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < vr && c < vc) v = ld16(DH + (int64_t)r * p.dh_row_bytes + c * 16);
-        st16(ldh + r * ld + c * 16, v);
-      }
+#pragma unroll
+    for (int i = 0; i < kDhChunks; ++i) {
+      const int q = threadIdx.x + i * TL::THREADS;
+      const int r = q / cpr, c = q - r * cpr;
+      st16(ldh + r * ld + c * 16, dh_reg[i]);
     }
     __syncthreads();
 #pragma unroll
