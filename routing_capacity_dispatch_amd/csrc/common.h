@@ -64,6 +64,11 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Wait for every vector memory operation of the wavefront (vmcnt(0); the
+// other counters left alone), as an instruction the compiler's own wait
+// placement takes into account, unlike a wait written in inline assembly
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Streaming store of data the next kernel reads once (nontemporal hint)
 __device__ __forceinline__ void st16_stream(void* p, const uint4& v) {
   __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));

@@ -426,7 +426,28 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
       const int r = q / cpr, c = q - r * cpr;
       // clamped address, result selected: no branch between the loads
       const uint4 v = ld16(DH + (int64_t)min(r, vr - 1) * p.dh_row_bytes + min(c, vc - 1) * 16);
-      dh_reg[i] = (r < vr) & (c < vc) ? v : make_uint4(0, 0, 0, 0);
+      dh_reg[i] = ((r < vr) & (c < vc)) ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // the output row of each 16-byte chunk this thread stores (modes 0, 1),
+  // read at the tile's start with every load in flight together, so the
+  // store loop holds no load (a load there makes each store wait for the
+  // previous one: stores count in the same vector memory counter)
+  constexpr int kOutCpr = (kSwiglu ? TL::BN / 2 : TL::BN) * 2 / 16;
+  constexpr int kOutIters = kMode == 2 ? 1 : TL::BM * kOutCpr / TL::THREADS;
+  static_assert(kMode == 2 || TL::BM * kOutCpr % TL::THREADS == 0, "whole chunks per thread");
+  int32_t out_row[kOutIters];
+  if constexpr (kMode != 2) {
+    const int vr = min(TL::BM, rows - m0);
+    if (p.c_index) {
+#pragma unroll
+      for (int i = 0; i < kOutIters; ++i) {
+        const int r = (int)(threadIdx.x + i * TL::THREADS) / kOutCpr;
+        out_row[i] = p.c_index[row0 + m0 + max(min(r, vr - 1), 0)];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kOutIters; ++i) out_row[i] = row0 + m0 + (int)(threadIdx.x + i * TL::THREADS) / kOutCpr;
     }
   }
   Acc<TL> acc;
@@ -509,13 +530,23 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
   else
     stage_bf16<TL>(acc, lds, ld);
   __syncthreads();
-  const int cpr = tile_cols * 2 / 16;
-  const int32_t* ci = p.c_index;
-  // the down-projection's rows are read once, by the combine
-  copy_rows<TL, !kSwiglu>(lds, ld, cpr, min(TL::BM, rows - m0), min(cpr, (cols - c0) * 2 / 16), [&](int r) {
-    const int64_t row = ci ? ci[row0 + m0 + r] : row0 + m0 + r;
-    return p.C + row * p.c_row_bytes + (int64_t)c0 * 2;
-  });
+  const int vr = min(TL::BM, rows - m0), vc = min(kOutCpr, (cols - c0) * 2 / 16);
+  // the row indices have long landed; one wait here, else the compiler
+  // waits for them inside the loop by counts that also cover the stores
+  wait_vm_all();
+#pragma unroll
+  for (int i = 0; i < kOutIters; ++i) {
+    const int q = threadIdx.x + i * TL::THREADS;
+    const int r = q / kOutCpr, c = q - r * kOutCpr;
+    if (r < vr && c < vc) {
+      const uint4 v = ld16(lds + r * ld + c * 16);
+      char* dst = p.C + (int64_t)out_row[i] * p.c_row_bytes + (int64_t)c0 * 2 + c * 16;
+      if constexpr (kSwiglu)
+        st16(dst, v);
+      else
+        st16_stream(dst, v);  // the down-projection's rows are read once, by the combine
+    }
+  }
 }
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

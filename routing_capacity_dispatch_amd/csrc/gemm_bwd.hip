@@ -47,8 +47,6 @@ constexpr int lds_bytes() {
   return TL::MAIN_LDS > TL::BM * (TL::BN * 2 + kStagePad) ? TL::MAIN_LDS : TL::BM * (TL::BN * 2 + kStagePad);
 }
 
-__device__ __forceinline__ int xcd_order(int bid, int nblocks) { return (bid & 7) * (nblocks >> 3) + (bid >> 3); }
-
 // kStream: nontemporal stores (outputs no later tile of the kernel reads)
 template <class TL, bool kStream = false, class RowPtr>
 __device__ __forceinline__ void copy_rows(const char* lds, int ld, int chunks_per_row, int valid_rows,
@@ -133,11 +131,31 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
     char* C = p.C + (int64_t)(row0 + m0) * p.c_row_bytes + (int64_t)n0 * 2;
     copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows_pad - m0), [&](int r) { return C + (int64_t)r * p.c_row_bytes; });
   } else {
+    // the pool slot of each row this thread stores, read before the staging
+    // with every load in flight together (a load in the store loop makes each
+    // store wait for the previous one: stores count in the same counter); not
+    // before the K loop, which is at the register limit
+    constexpr int kOutIters = TL::BM * cpr / TL::THREADS;
+    static_assert(TL::BM * cpr % TL::THREADS == 0, "whole chunks per thread");
+    const int vr = min(TL::BM, rows - m0);  // may be <= 0: a tile of padding rows stores nothing
+    int32_t out_row[kOutIters];
+#pragma unroll
+    for (int i = 0; i < kOutIters; ++i) {
+      const int r = (int)(threadIdx.x + i * TL::THREADS) / cpr;
+      out_row[i] = p.c_index[row0 + m0 + max(min(r, vr - 1), 0)];
+    }
     stage<TL>(acc, lds, ld, 0);
     __syncthreads();
-    const int32_t* ci = p.c_index + row0 + m0;
-    copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows - m0),
-                  [&](int r) { return p.C + (int64_t)ci[r] * p.c_row_bytes + (int64_t)n0 * 2; });
+    // one wait for the indices, else the compiler waits for them inside the
+    // loop by counts that also cover the stores
+    wait_vm_all();
+#pragma unroll
+    for (int i = 0; i < kOutIters; ++i) {
+      const int q = threadIdx.x + i * TL::THREADS;
+      const int r = q / cpr, c = q - r * cpr;
+      if (r < vr)
+        st16(p.C + (int64_t)out_row[i] * p.c_row_bytes + (int64_t)n0 * 2 + c * 16, ld16(lds + r * ld + c * 16));
+    }
   }
 }
 
