@@ -85,8 +85,8 @@ __global__ __launch_bounds__(64) void bwd_gidx_ragged_kernel(const int32_t* __re
 
 // dst row i = the pool row gidx[i] (block = i / block_rows at block_bytes
 // apart, rows row_bytes apart inside a block), or zeros where gidx[i] < 0.
-// One wavefront per row (grid-stride over rows), six 16-byte chunks per
-// lane in flight.
+// One wavefront per row (the grid covers the bound on the row count), six
+// 16-byte chunks per lane in flight.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src, int block_rows,
                                                           int64_t block_bytes, int64_t row_bytes,
                                                           const int32_t* __restrict__ gidx,
@@ -94,28 +94,28 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
   constexpr int CPL = 6;
   const int lane = threadIdx.x & 63;
   const int cpr = (int)(row_bytes / 16);
-  const int64_t n = *nrows;
-  for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < n; i += (int64_t)gridDim.x * 4) {
-    const int fi = gidx[i];
-    const char* srow = nullptr;
-    if (fi >= 0) {
-      const int blk = fi / block_rows;
-      srow = src + blk * block_bytes + (int64_t)(fi - blk * block_rows) * row_bytes;
-    }
-    char* drow = dst + i * row_bytes;
-    for (int c0 = 0; c0 < cpr; c0 += 64 * CPL) {
-      uint4 v[CPL];
+  // one row per wavefront (the grid covers the bound on the row count), so
+  // no row's loads wait behind an earlier row's stores
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= *nrows) return;
+  const int fi = gidx[i];
+  char* drow = dst + i * row_bytes;
+  if (fi < 0) {  // a padding row: zeros
+    for (int c = lane; c < cpr; c += 64) st16(drow + (int64_t)c * 16, make_uint4(0, 0, 0, 0));
+    return;
+  }
+  const int blk = fi / block_rows;
+  const char* srow = src + blk * block_bytes + (int64_t)(fi - blk * block_rows) * row_bytes;
+  for (int c0 = 0; c0 < cpr; c0 += 64 * CPL) {
+    uint4 v[CPL];
+    // chunk indices clamped (not stored past the row's end): no branch
+    // between the loads
 #pragma unroll
-      for (int u = 0; u < CPL; ++u) {
-        const int c = c0 + u * 64 + lane;
-        v[u] = make_uint4(0, 0, 0, 0);
-        if (srow && c < cpr) v[u] = ld16(srow + (int64_t)c * 16);
-      }
+    for (int u = 0; u < CPL; ++u) v[u] = ld16(srow + (int64_t)min(c0 + u * 64 + lane, cpr - 1) * 16);
 #pragma unroll
-      for (int u = 0; u < CPL; ++u) {
-        const int c = c0 + u * 64 + lane;
-        if (c < cpr) st16(drow + (int64_t)c * 16, v[u]);
-      }
+    for (int u = 0; u < CPL; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < cpr) st16(drow + (int64_t)c * 16, v[u]);
     }
   }
 }
@@ -126,8 +126,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 // then a butterfly over the wavefront) and the row g[t, j] * dy[t] goes to
 // the pool slot the forward read o[t, j] from.  A dropped assignment gets
 // d_gates = 0 and no row.  Lanes j < k load the token's assignments at once;
-// the o rows are then read two at a time.  dy and o are read once, so their
-// loads carry the nontemporal hint.
+// the o rows are then read two at a time, and the g dy rows stored after the
+// last of them.  dy and o are read once, so their loads carry the
+// nontemporal hint.
 template <int kMaxChunks, bool kRowOf>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   } else {
     const int rs = a.recv_slot[q], e = a.topk[q], ps = a.pool_slot[q];
     // (& rather than &&: no short-circuit branch to sink a load into)
-    row = (rs >= 0) & (e >= 0) & (e < a.E) & (ps >= 0) & (ps < a.cap_send) ? (w * a.P + e / epp) * a.cap_send + ps : -1;
+    row = ((rs >= 0) & (e >= 0) & (e < a.E) & (ps >= 0) & (ps < a.cap_send)) ? (w * a.P + e / epp) * a.cap_send + ps
+                                                                              : -1;
   }
   const float gq = a.gates[q];
   if (lane >= k) row = -1;
@@ -168,8 +170,6 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
       const int j1 = j + 1 < k ? j + 1 : j;
       const bool k0 = readlane64(row, j) >= 0;
       const bool k1 = j + 1 < k && readlane64(row, j1) >= 0;
-      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), j));
-      const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), j1));
       const int64_t rb0 = readlane64(r_l, j) * a.row_bytes, rb1 = readlane64(r_l, j1) * a.row_bytes;
       const char* o0 = static_cast<const char*>(a.expert_out) + rb0;
       const char* o1 = static_cast<const char*>(a.expert_out) + rb1;
@@ -185,21 +185,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
       for (int i = 0; i < kMaxChunks; ++i) {
         const int c = i * 64 + lane;
         if (c >= chunks) continue;
-        float f[8], out[8];
+        float f[8];
         unpack(v0[i], f, bf16_t{});
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          s0 = fmaf(dy[i][x], f[x], s0);
-          out[x] = g0 * dy[i][x];
-        }
-        if (k0) st16(static_cast<char*>(a.d_expert_out) + rb0 + (int64_t)c * 16, pack(out, bf16_t{}));
+        for (int x = 0; x < 8; ++x) s0 = fmaf(dy[i][x], f[x], s0);
         unpack(v1[i], f, bf16_t{});
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          s1 = fmaf(dy[i][x], f[x], s1);
-          out[x] = g1 * dy[i][x];
-        }
-        if (k1) st16(static_cast<char*>(a.d_expert_out) + rb1 + (int64_t)c * 16, pack(out, bf16_t{}));
+        for (int x = 0; x < 8; ++x) s1 = fmaf(dy[i][x], f[x], s1);
       }
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) {
@@ -208,6 +200,22 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
       }
       if (lane == j) dg = k0 ? s0 : 0.0f;
       if (lane == j + 1) dg = k1 ? s1 : 0.0f;
+    }
+    // the rows g_j dy go out after every load of the token, so no load waits
+    // behind a store (stores count in the same vector memory counter)
+    for (int j = 0; j < k; ++j) {
+      if (readlane64(row, j) < 0) continue;
+      const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), j));
+      char* d = static_cast<char*>(a.d_expert_out) + readlane64(r_l, j) * a.row_bytes;
+#pragma unroll
+      for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = i * 64 + lane;
+        if (c >= chunks) continue;
+        float out[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) out[x] = gj * dy[i][x];
+        st16(d + (int64_t)c * 16, pack(out, bf16_t{}));
+      }
     }
   }
   if (lane < k) a.d_gates[t * k + lane] = dg;
@@ -273,8 +281,9 @@ hipError_t launch_gather_rows(const void* src, int block_rows, int64_t block_byt
                               const int32_t* gidx, const int32_t* nrows, int64_t max_rows, void* dst,
                               hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  const int64_t want = (max_rows + 3) / 4;  // four rows per block
-  const unsigned blocks = (unsigned)(want < 16384 ? want : 16384);
+  const int64_t want = (max_rows + 3) / 4;  // four rows per block, one per wavefront
+  if (want > 0x7fffffff) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)want;
   gather_rows_kernel<<<blocks, 256, 0, s>>>(static_cast<const char*>(src), block_rows, block_bytes, row_bytes,
                                             gidx, nrows, static_cast<char*>(dst));
   return hipGetLastError();

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a, const char
   const int64_t q = t * k + min(lane, k - 1);
   const int ps = a.pool_slot[q], e = a.topk[q];
   const int64_t off = (w * a.P + e / epp) * a.block_bytes + (int64_t)ps * a.row_bytes;  // used only if kept
-  char* dst = (lane < k) & (ps >= 0) ? a.pools + off : nullptr;
+  char* dst = ((lane < k) & (ps >= 0)) ? a.pools + off : nullptr;
   if (chunks > 512) {
     scatter_row(src, dst, k, a.row_bytes);
     return;
