@@ -112,6 +112,41 @@ def summarize_pmc(fetch_csv, write_csv, stage, workload, copy_bytes, out_path, c
     print(json.dumps(rec))
 
 
+def summarize_clock(csv_path, xcds, simds, min_us, nominal_ghz=2.4):
+    """Per library kernel, from one rocprofv3 --pmc file with GRBM_GUI_ACTIVE
+    and SQ_VALU_MFMA_BUSY_CYCLES (mean over its dispatches): the duration,
+    the shader clock (GUI-active cycles, which the counter sums over the
+    XCDs, per nanosecond) and the fraction of SIMD cycles the matrix cores
+    were busy.  Prints a markdown table of the kernels of at least min_us
+    (the counter window of a short dispatch holds more than its run, so its
+    clock reads high)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        name = r["Kernel_Name"]
+        if "at::" in name or "copyBuffer" in name or "amd_rocclr" in name:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"name": name, "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    kern = {}
+    for d in per.values():
+        if "GRBM_GUI_ACTIVE" not in d or "SQ_VALU_MFMA_BUSY_CYCLES" not in d or d["ns"] < min_us * 1e3:
+            continue
+        kern.setdefault(d["name"], []).append(d)
+    print(f"| kernel | dispatches | avg µs | clock GHz | MFMA busy | clock-limited bf16 peak TFLOP/s |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, ds in sorted(kern.items(), key=lambda kv: -sum(x["ns"] for x in kv[1])):
+        ns = sum(x["ns"] for x in ds) / len(ds)
+        gui = sum(x["GRBM_GUI_ACTIVE"] for x in ds) / len(ds) / xcds
+        mfma = sum(x["SQ_VALU_MFMA_BUSY_CYCLES"] for x in ds) / len(ds)
+        ghz = gui / ns
+        busy = mfma / (gui * simds) if gui else 0.0
+        short = name.replace("moe::(anonymous namespace)::", "")
+        short = short if len(short) <= 80 else short[:77] + "..."
+        print(f"| `{short}` | {len(ds)} | {ns / 1e3:.1f} | {ghz:.2f} | {busy:.3f} | "
+              f"{2500.0 * ghz / nominal_ghz:.0f} |")
+
+
 def stage_work(w, kept, sent, dropless=False, backward=False, bias_bins=0):
     """Algorithmic flops (MFMA stages) or bytes (HBM stages) per launch."""
     eb = 2 if w.dtype == "bf16" else 4
@@ -466,7 +501,16 @@ def main():
                          "--pmc counter files and exit")
     ap.add_argument("--stage", default="expert_gate_up", help="stage for --summarize-pmc")
     ap.add_argument("--pmc-command", default="", help="command recorded by --summarize-pmc")
+    ap.add_argument("--summarize-clock", metavar="COUNTER_CSV",
+                    help="print each kernel's clock and matrix-core busy fraction from a rocprofv3 "
+                         "--pmc file of GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES, and exit")
+    ap.add_argument("--xcds", type=int, default=8, help="XCDs the GUI-active counter sums over")
+    ap.add_argument("--simds", type=int, default=1024, help="SIMDs of the device (4 per CU)")
+    ap.add_argument("--min-us", type=float, default=400.0, help="shortest kernel --summarize-clock lists")
     args = ap.parse_args()
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock, args.xcds, args.simds, args.min_us)
+        return
     run_name = (args.workload + ("_dropless" if args.dropless else "") + ("_backward" if args.backward else "")
                 + ("_bias" if args.bias_update else ""))
     if args.cpu_tokens is None and not args.recv_share:
