@@ -36,6 +36,10 @@ using DenseTile = core::Tile<256, 256, 4, 2, 64, 2>;
 // a third B stage, all 160 KB of LDS: the shared SwiGLU GEMM and single-segment dense GEMMs
 using DenseTile3B = core::Tile<256, 256, 4, 2, 64, 2, 3>;
 using ExpertTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;
+// experts with thousands of rows each: the dense GEMMs' 256-row tile (more
+// MFMA work per staged operand byte; an expert's padding is then a few per cent)
+using ExpertTileTall = core::Tile<256, 256, 4, 2, 64, 2, 3>;
+static_assert(ExpertTileTall::BN == ExpertTile::BN, "both expert tiles share the N tiling");
 // fp32 output (the router logits): 4 wavefronts of 64 x 48; E = 384 columns
 // are four N tiles, so the Marin-shaped router GEMM is 512 tiles, two per CU
 using RouterTile = core::Tile<128, 96, 2, 2, 64, 2>;
@@ -554,19 +558,25 @@ inline int pad8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 }  // namespace
 
-int ragged_tile_rows() { return ExpertTile::BM; }
+int ragged_tile_rows(bool tall) { return tall ? ExpertTileTall::BM : ExpertTile::BM; }
 int ragged_gate_up_cols() { return ExpertTile::BN / 2; }
 int ragged_down_cols() { return ExpertTile::BN; }
 
-hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
+hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, bool tall, hipStream_t s) {
   if (max_entries <= 0) return hipSuccess;
-  ragged_gemm_kernel<ExpertTile, 1><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
+  if (tall)
+    ragged_gemm_kernel<ExpertTileTall, 1><<<pad8(max_entries), ExpertTileTall::THREADS, 0, s>>>(g);
+  else
+    ragged_gemm_kernel<ExpertTile, 1><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
 
-hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s) {
+hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, bool tall, hipStream_t s) {
   if (max_entries <= 0) return hipSuccess;
-  ragged_gemm_kernel<ExpertTile, 0><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
+  if (tall)
+    ragged_gemm_kernel<ExpertTileTall, 0><<<pad8(max_entries), ExpertTileTall::THREADS, 0, s>>>(g);
+  else
+    ragged_gemm_kernel<ExpertTile, 0><<<pad8(max_entries), ExpertTile::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
 

@@ -181,12 +181,13 @@ struct RaggedGemm {
   char* H;
   int64_t h_row_bytes;
 };
-// M rows per tile and N columns (features for the SwiGLU) per tile.
-int ragged_tile_rows();
+// M rows per tile (192, or 256 with `tall`: for experts of thousands of rows)
+// and N columns (features for the SwiGLU) per tile, the same for both.
+int ragged_tile_rows(bool tall);
 int ragged_gate_up_cols();
 int ragged_down_cols();
-hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
-hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, hipStream_t s);
+hipError_t launch_ragged_gate_up_bf16(const RaggedGemm& g, int64_t max_entries, bool tall, hipStream_t s);
+hipError_t launch_ragged_down_bf16(const RaggedGemm& g, int64_t max_entries, bool tall, hipStream_t s);
 // The backward's recompute of the SwiGLU pre-activations a = u W_g^T,
 // b = u W_u^T (fp32, never stored) with the SwiGLU backward in the
 // epilogue: from dh (g.dH) it writes da | db (g.C) and h (g.H), bf16.

@@ -66,11 +66,21 @@ int64_t capacity(int64_t num, int64_t den, int64_t Tw, int64_t k, int64_t n) {
   return (int64_t)((a + b - 1) / b);
 }
 
+// The routed experts' grouped GEMMs take 256-row tiles instead of 192-row
+// ones when an expert's expected rows ceil(T k / E) reach kTallRows: both
+// tiles then pad an expert by a few per cent at most, and the taller tile
+// does more MFMA work per staged operand byte.  A function of the config
+// only, so the plan's workspace sizes and every launch agree.
+constexpr int64_t kTallRows = 4096;
+bool tall_tiles(const moe_config* c) {
+  return ceil_div(c->T * (int64_t)c->top_k, c->n_experts) >= kTallRows;
+}
+
 // Upper bounds of the ragged GEMMs' tile lists: expert e has
 // ceil(count_e / bm) <= count_e / bm + 1 M tiles.
 void dropless_entries(const moe_config* c, int64_t* ent0, int64_t* ent1) {
   const int64_t n = c->T * (int64_t)c->top_k;
-  const int64_t bm = moe::ragged_tile_rows();
+  const int64_t bm = moe::ragged_tile_rows(tall_tiles(c));
   const int64_t mt = ceil_div(n, bm) + c->n_experts;
   *ent0 = mt * ceil_div(c->d_ff, moe::ragged_gate_up_cols());
   *ent1 = mt * ceil_div(c->d_latent, moe::ragged_down_cols());
@@ -79,7 +89,7 @@ void dropless_entries(const moe_config* c, int64_t* ent0, int64_t* ent1) {
 // Tile-list bounds of the capped path's grouped GEMMs: expert e holds at
 // most max_rows kept rows, and sum_e count_e <= E * max_rows.
 void capped_entries(const moe_config* c, int64_t max_rows, int64_t* ent0, int64_t* ent1) {
-  const int64_t bm = moe::ragged_tile_rows();
+  const int64_t bm = moe::ragged_tile_rows(tall_tiles(c));
   const int64_t E = c->n_experts;
   const int64_t per = ceil_div(max_rows, bm);
   const int64_t mt = per * E < ceil_div(E * max_rows, bm) + E ? per * E : ceil_div(E * max_rows, bm) + E;
@@ -354,7 +364,8 @@ moe_status run_experts(const moe_config* c, const moe_plan& p, const void* pools
     hipError_t e = moe::launch_expert_gidx(bank_rows, expert_count, E, c->n_pools, c->n_waves, p.cap_send,
                                            p.cap_recv, offsets, gidx, s);
     if (e == hipSuccess)
-      e = moe::launch_ragged_tiles(offsets, E, moe::ragged_tile_rows(), tn0, tn1, list0, list1, ntiles, s);
+      e = moe::launch_ragged_tiles(offsets, E, moe::ragged_tile_rows(tall_tiles(c)), tn0, tn1, list0, list1,
+                                   ntiles, s);
     if (e == hipSuccess && m) e = m->mark(s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     moe::RaggedGemm g{};
@@ -373,7 +384,7 @@ moe_status run_experts(const moe_config* c, const moe_plan& p, const void* pools
     g.K = c->d_latent;
     g.C = H;
     g.c_row_bytes = (int64_t)c->d_ff * p.elem_bytes;
-    e = moe::launch_ragged_gate_up_bf16(g, ent0, s);
+    e = moe::launch_ragged_gate_up_bf16(g, ent0, tall_tiles(c), s);
     if (e == hipSuccess && m) e = m->mark(s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     moe::RaggedGemm d{};
@@ -389,7 +400,7 @@ moe_status run_experts(const moe_config* c, const moe_plan& p, const void* pools
     d.C = static_cast<char*>(expert_out);
     d.c_row_bytes = p.row_bytes;
     d.c_index = gidx;
-    e = moe::launch_ragged_down_bf16(d, ent1, s);
+    e = moe::launch_ragged_down_bf16(d, ent1, tall_tiles(c), s);
     if (e == hipSuccess && m) e = m->mark(s);
     return hip_status(e);
   }
@@ -803,8 +814,8 @@ moe_status run_experts_dropless(const moe_config* c, const moe_plan& p, const vo
   char* H = static_cast<char*>(cv.take(n * c->d_ff * p.elem_bytes));
   const int tn0 = (int)ceil_div(c->d_ff, moe::ragged_gate_up_cols());
   const int tn1 = (int)ceil_div(c->d_latent, moe::ragged_down_cols());
-  hipError_t e = moe::launch_ragged_tiles(offsets, c->n_experts, moe::ragged_tile_rows(), tn0, tn1, list0,
-                                          list1, ntiles, s);
+  hipError_t e = moe::launch_ragged_tiles(offsets, c->n_experts, moe::ragged_tile_rows(tall_tiles(c)), tn0, tn1,
+                                          list0, list1, ntiles, s);
   if (e == hipSuccess && m) e = m->mark(s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   moe::RaggedGemm g{};
@@ -821,7 +832,7 @@ moe_status run_experts_dropless(const moe_config* c, const moe_plan& p, const vo
   g.N = 0;
   g.C = H;
   g.c_row_bytes = (int64_t)c->d_ff * p.elem_bytes;
-  e = moe::launch_ragged_gate_up_bf16(g, ent0, s);
+  e = moe::launch_ragged_gate_up_bf16(g, ent0, tall_tiles(c), s);
   if (e == hipSuccess && m) e = m->mark(s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   moe::RaggedGemm d{};
@@ -838,7 +849,7 @@ moe_status run_experts_dropless(const moe_config* c, const moe_plan& p, const vo
   d.N = c->d_latent;
   d.C = static_cast<char*>(out);
   d.c_row_bytes = p.row_bytes;
-  e = moe::launch_ragged_down_bf16(d, ent1, s);
+  e = moe::launch_ragged_down_bf16(d, ent1, tall_tiles(c), s);
   if (e == hipSuccess && m) e = m->mark(s);
   return hip_status(e);
 }
@@ -1072,7 +1083,7 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const BwdRows
   // one M-tile structure serves the recompute (expert tile) and dh (dgrad
   // tile) lists, so the two tiles must have the same row count
   const int bm = moe::bwd_dgrad_rows();
-  if (bm != moe::ragged_tile_rows()) return MOE_ERR_UNSUPPORTED;
+  if (bm != moe::ragged_tile_rows(false)) return MOE_ERR_UNSUPPORTED;
   hipError_t e = ragged ? moe::launch_bwd_layout_ragged(src.expert_offsets, E, p.dropless_rows, counts, offsets,
                                                          gidx, s)
                         : moe::launch_bwd_layout(src.bank_rows, src.expert_count, E, c->n_pools, c->n_waves,

@@ -81,6 +81,7 @@ EXPERT_CASES = [
     ("mid", 4096, 64, 8, 0.01, 512, 512),     # ~512 rows per expert: 3 M tiles
     ("skewed", 333, 12, 3, 2.0, 192, 320),    # empty experts, partial feature tile
     ("marin", 16384, 384, 8, 0.0, 3072, 3072),
+    ("tall", 16384, 4, 2, 0.0, 256, 256),     # 8192 rows per expert: 256-row expert tiles
 ]
 
 
@@ -161,7 +162,8 @@ def test_forward_dropless_mid(seed):
 
 
 @pytest.mark.parametrize("over", [dict(T=1), dict(T=257), dict(T=1000, n_experts=4, n_pools=1, top_k=1),
-                                  dict(T=512, n_shared=0), dict(T=300, top_k=16)])
+                                  dict(T=512, n_shared=0), dict(T=300, top_k=16),
+                                  dict(T=8192, n_experts=4, n_pools=4, top_k=2)])  # 256-row expert tiles
 def test_forward_dropless_special(over):
     d = dev()
     say("forward dropless special", over)

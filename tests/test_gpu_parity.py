@@ -195,6 +195,9 @@ EXPERT_CASES = [
     ("bands", 4096, 2, 1, 1, 1, 256, 256, "bf16", 0.0),
     # ... and 12, 18 and 16 M tiles over three waves, with receiver drops
     ("bands_w3", 9000, 3, 1, 1, 3, 128, 256, "bf16", 0.3),
+    # ceil(T k / E) >= 4096 expected rows per expert: the 256-row expert tile
+    ("tall", 16384, 4, 1, 2, 1, 256, 256, "bf16", 0.0),
+    ("tall_w3", 12288, 3, 1, 1, 3, 128, 256, "bf16", 0.3),
 ]
 
 
@@ -330,6 +333,14 @@ def test_forward_special_cases(over):
         assert a["sender_dropped"] == w.T * w.top_k
     if over.get("recv_cap") == (0, 1):
         assert a["receiver_dropped"] == w.T * w.top_k
+
+
+def test_forward_bf16_tall_expert_tiles():
+    # 8192 tokens x top-2 over 4 experts: 4096 expected rows per expert, so the
+    # routed GEMMs run on 256-row tiles
+    d = dev()
+    say("forward bf16 tall expert tiles")
+    _check_forward(synth.workload("mid_bf16").replace(T=8192, n_experts=4, n_pools=4, top_k=2), 5, d)
 
 
 def test_forward_bf16_single_expert_and_empty():
