@@ -7,8 +7,11 @@
 // Tile shapes: 256 x 256 with 8 wavefronts (64 x 128 each) for the dense
 // contractions, whose M (tokens) and N are large; 192 x 256 with 8
 // wavefronts (96 x 64 each) for the routed experts, whose ~341 rows per
-// expert fit two 192-row tiles with little padding.  The experts' weight
-// tiles stream from HBM once each, so they get a third LDS stage.
+// expert fit two 192-row tiles with little padding, and the 256 x 256 tile
+// for them too when experts hold thousands of rows each.  In an expert's
+// last tile each wavefront computes only the 16-row blocks of its band that
+// hold rows.  The experts' weight tiles stream from HBM once each, so they
+// get a third LDS stage.
 //
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
 // every kernel maps its linear block index to a tile such that one XCD gets
@@ -31,6 +34,7 @@ using core::load_row;
 using core::mainloop;
 using core::RowSrc;
 using core::uniform_ptr;
+using core::with_row_blocks;
 
 using DenseTile = core::Tile<256, 256, 4, 2, 64, 2>;
 // a third B stage, all 160 KB of LDS: the shared SwiGLU GEMM and single-segment dense GEMMs
@@ -454,10 +458,19 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
       for (int i = 0; i < kOutIters; ++i) out_row[i] = row0 + m0 + (int)(threadIdx.x + i * TL::THREADS) / kOutCpr;
     }
   }
-  Acc<TL> acc;
-  acc.zero();
-  mainloop<TL>(a_src, b_src, p.K / TL::BK, lds, acc);
+  // this wavefront's band of the tile's rows: its MFMAs (and fragment
+  // reads) cover only the 16-row blocks that hold some of the expert's
+  // rows (every row the tile stores), so an expert's last tile spends no
+  // matrix-core work on whole blocks of padding; loads, barriers and LDS
+  // stages are the same in every variant
+  const int band = min(TL::BM, rows - m0) - (wave / TL::WGN) * TL::WM;
+  const int mie = __builtin_amdgcn_readfirstlane((min(max(band, 1), TL::WM) + 15) >> 4);
   if constexpr (kMode == 2) {
+    with_row_blocks<TL>(mie, [&](auto view) {
+    using TV = decltype(view);
+    Acc<TV> acc;
+    acc.zero();
+    mainloop<TV>(a_src, b_src, p.K / TL::BK, lds, acc);
     static_assert(((TL::BM * ((TL::BN / 2) * 2 + kStagePad) + 1023) & ~1023) + TL::BM * ((TL::BN / 2) * 2 + kStagePad) <=
                       lds_bytes<TL>(),
                   "output staging and the dh tile fit the kernel's LDS");
@@ -482,12 +495,12 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
     }
     __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < TL::MI; ++mi)
+    for (int mi = 0; mi < TV::MI; ++mi)
 #pragma unroll
       for (int q = 0; q < TL::NI / 2; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = acc_row<TL>(wm, mi, lane, r);
+          const int row = acc_row<TV>(wm, mi, lane, r);
           const int col = wn * (TL::WN / 2) + q * 16 + (lane & 15);
           float da = 0.0f, db = 0.0f, h = 0.0f;
           if (m0 + row < rows && c0 + col < p.F) {
@@ -509,12 +522,12 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
     for (int pass = 1; pass <= 2; ++pass) {
       __syncthreads();
 #pragma unroll
-      for (int mi = 0; mi < TL::MI; ++mi)
+      for (int mi = 0; mi < TV::MI; ++mi)
 #pragma unroll
         for (int q = 0; q < TL::NI / 2; ++q)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = acc_row<TL>(wm, mi, lane, r);
+            const int row = acc_row<TV>(wm, mi, lane, r);
             const int col = wn * (TL::WN / 2) + q * 16 + (lane & 15);
             *reinterpret_cast<uint16_t*>(lds + row * ld + col * 2) =
                 static_cast<uint16_t>(__float_as_uint(acc.v[mi][2 * q][r]) >> (pass == 1 ? 0 : 16));
@@ -524,15 +537,22 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
       const int64_t rb = pass == 1 ? p.c_row_bytes : p.h_row_bytes;
       copy_rows<TL>(lds, ld, cpr, vr, vc, [&](int r) { return dst + (int64_t)r * rb; });
     }
+    });
     return;
   }
   const int cols = kSwiglu ? p.F : p.N;
   const int tile_cols = kSwiglu ? TL::BN / 2 : TL::BN;
   const int ld = tile_cols * 2 + kStagePad;
-  if (kSwiglu)
-    stage_swiglu_bf16<TL>(acc, lds, ld);
-  else
-    stage_bf16<TL>(acc, lds, ld);
+  with_row_blocks<TL>(mie, [&](auto view) {
+    using TV = decltype(view);
+    Acc<TV> acc;
+    acc.zero();
+    mainloop<TV>(a_src, b_src, p.K / TL::BK, lds, acc);
+    if (kSwiglu)
+      stage_swiglu_bf16<TV>(acc, lds, ld);
+    else
+      stage_bf16<TV>(acc, lds, ld);
+  });
   __syncthreads();
   const int vr = min(TL::BM, rows - m0), vc = min(kOutCpr, (cols - c0) * 2 / 16);
   // the row indices have long landed; one wait here, else the compiler

@@ -37,6 +37,7 @@ using core::load_row;
 using core::mainloop;
 using core::RowSrc;
 using core::uniform_ptr;
+using core::with_row_blocks;
 
 using DgradTile = core::Tile<192, 256, 2, 4, 64, 2, 3>;  // the weights stream: a third B stage
 using WgradTile = core::Tile<256, 256, 4, 2, 32, 4>;
@@ -101,7 +102,14 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
   const int m0 = mt * TL::BM, n0 = nt * TL::BN;
   if (m0 >= rows_pad) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Acc<TL> acc;
+  // this wavefront's band of the tile's rows: MFMAs only for the 16-row
+  // blocks that hold a row the tile stores (dh: every padded row, whose
+  // zeros later contractions read; du: the expert's rows)
+  const int band = min(TL::BM, (kMode == 0 ? rows_pad : rows) - m0) - (wave / TL::WGN) * TL::WM;
+  const int mie = __builtin_amdgcn_readfirstlane((min(max(band, 1), TL::WM) + 15) >> 4);
+  with_row_blocks<TL>(mie, [&](auto view) {
+  using TV = decltype(view);
+  Acc<TV> acc;
   acc.zero();
   const char* A = uniform_ptr(p.A + (int64_t)row0 * p.a_row_bytes);
   for (int seg = 0; seg < (kMode == 1 ? 2 : 1); ++seg) {
@@ -120,13 +128,13 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
       b_src.base[i] = W;
       b_src.off[i] = (uint32_t)(kr * p.N * 2) + kload_col<TL::BN>(kr, lane);
     }
-    mainloop<TL, true, false, true>(a_src, b_src, p.K / TL::BK, lds, acc, TL::RB, (int64_t)64 * p.N * 2);
+    mainloop<TV, true, false, true>(a_src, b_src, p.K / TL::BK, lds, acc, TL::RB, (int64_t)64 * p.N * 2);
   }
   constexpr int ld = TL::BN * 2 + kStagePad;
   constexpr int cpr = TL::BN * 2 / 16;
   if constexpr (kMode == 0) {
     // dh rows, padding rows included (their do rows are zero)
-    stage<TL>(acc, lds, ld, 0);
+    stage<TV>(acc, lds, ld, 0);
     __syncthreads();
     char* C = p.C + (int64_t)(row0 + m0) * p.c_row_bytes + (int64_t)n0 * 2;
     copy_rows<TL>(lds, ld, cpr, min(TL::BM, rows_pad - m0), [&](int r) { return C + (int64_t)r * p.c_row_bytes; });
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
       const int r = (int)(threadIdx.x + i * TL::THREADS) / cpr;
       out_row[i] = p.c_index[row0 + m0 + max(min(r, vr - 1), 0)];
     }
-    stage<TL>(acc, lds, ld, 0);
+    stage<TV>(acc, lds, ld, 0);
     __syncthreads();
     // one wait for the indices, else the compiler waits for them inside the
     // loop by counts that also cover the stores
@@ -157,6 +165,7 @@ __global__ __launch_bounds__(DgradTile::THREADS) void dgrad_kernel(BwdDgrad p) {
         st16(p.C + (int64_t)out_row[i] * p.c_row_bytes + (int64_t)n0 * 2 + c * 16, ld16(lds + r * ld + c * 16));
     }
   }
+  });
 }
 
 // ------------------------------------------------------------------ wgrad

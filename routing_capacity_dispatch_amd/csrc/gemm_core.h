@@ -638,6 +638,26 @@ __device__ __forceinline__ void mainloop(const RowSrc<TL::A_INS>& a_src, const R
   __syncthreads();
 }
 
+// A wavefront's view of tile TL that computes only its first MIe 16-row
+// blocks (every other constant, the loads and the LDS layout unchanged).
+template <class TL, int MIe>
+struct RowBlocks : TL {
+  static_assert(MIe >= 1 && MIe <= TL::MI, "1 .. MI row blocks");
+  static constexpr int MI = MIe;
+};
+
+// f(RowBlocks<TL, m>{}) with m = clamp(mie, 1, TL::MI): one compile-time
+// variant per row-block count, chosen once per tile (mie wave-uniform).
+template <class TL, int M = TL::MI, class F>
+__device__ __forceinline__ void with_row_blocks(int mie, F&& f) {
+  if constexpr (M == 1)
+    f(RowBlocks<TL, 1>{});
+  else if (mie >= M)
+    f(RowBlocks<TL, M>{});
+  else
+    with_row_blocks<TL, M - 1>(mie, f);
+}
+
 // Tile coordinates of register r of block (mi, ni) for this lane.
 template <class TL>
 __device__ __forceinline__ int acc_row(int wm, int mi, int lane, int r) {
