@@ -64,14 +64,46 @@ KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "di
 BIAS_SOURCES = ["bias.hip", "common.h"]
 
 
-def kernel_source_hash(run_name=""):
+def code_only(text):
+    """C/C++ source without its comments and with whitespace runs collapsed
+    (string and character literals kept): what the compiler reads, so that
+    a comment edit leaves the source hash unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def source_hash(paths):
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "routing_capacity_dispatch_amd", "csrc")
-    for f in (BIAS_SOURCES if run_name.endswith("_bias") else KERNEL_SOURCES):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    for path in paths:
+        with open(path, encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
+            h.update(b"\0")
     return h.hexdigest()
+
+
+def kernel_source_hash(run_name=""):
+    csrc = os.path.join(ROOT, "routing_capacity_dispatch_amd", "csrc")
+    return source_hash(os.path.join(csrc, f)
+                       for f in (BIAS_SOURCES if run_name.endswith("_bias") else KERNEL_SOURCES))
 
 
 def summarize_pmc(fetch_csv, write_csv, stage, workload, copy_bytes, out_path, command):

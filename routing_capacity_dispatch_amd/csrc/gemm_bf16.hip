@@ -203,7 +203,7 @@ struct SegK {
 // One K range (the latent projection), or K ranges joined as SegK
 // describes (Seg = true: ktiles K tiles over all of them; the one-range
 // kernel reads its K from the segment): the mid-tile barrier schedule with
-// a third B stage.  A few registers spill around the K loop, none inside it.
+// a third B stage.
 template <bool Seg>
 __device__ __forceinline__ void dense1_body(const GemmDense& g, const SegK& bk, int ktiles, int tiles_m,
                                             int tiles_n) {

@@ -79,3 +79,16 @@ def test_summarize_pmc(bench, tmp_path, capsys):
     # mean 2000 KiB fetched x 2 + mean 200 KiB written x 1
     assert rec["bytes_per_launch"] == pytest.approx((2000 * 2 + 200) * 1024.0)
     assert rec["source_sha256"] == bench.kernel_source_hash("marin_16k")
+
+
+def test_source_hash_ignores_comments_only(bench, tmp_path):
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text('// header\nint f(int x) { return x + 1; }  /* trailing */\nconst char* s = "// kept";\n')
+    b.write_text('/* another header */\nint f(int x) {\n  return x + 1;  // same code\n}\nconst char* s = "// kept";\n')
+    c.write_text('// header\nint f(int x) { return x + 2; }\nconst char* s = "// kept";\n')
+    assert bench.source_hash([a]) == bench.source_hash([b])
+    assert bench.source_hash([a]) != bench.source_hash([c])
+    # a comment marker inside a string literal is code
+    d = tmp_path / "d.hip"
+    d.write_text('// header\nint f(int x) { return x + 1; }\nconst char* s = "// changed";\n')
+    assert bench.source_hash([a]) != bench.source_hash([d])
