@@ -57,10 +57,10 @@ STAGE_KERNEL = {
     "bias_quantile": ("quantile_kernel",),
 }
 COPY_KERNEL = ("copyBuffer",)
-# sources of the GEMM kernels: a measured traffic figure is used only while
-# they are unchanged
-KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h", "combine.hip", "dispatch.hip",
-                  "gemm_bwd.hip", "backward.hip", "ragged.hip", "route.hip"]
+# sources of the kernel whose traffic the forward, dropless and backward lines
+# report (ragged_gemm_kernel: the routed gate/up GEMM, and the backward's
+# recompute): a measured traffic figure is used only while they are unchanged
+KERNEL_SOURCES = ["gemm_core.h", "gemm_bf16.hip", "common.h"]
 BIAS_SOURCES = ["bias.hip", "common.h"]
 
 

@@ -262,11 +262,13 @@ __device__ __forceinline__ void wgrad_interleave() {
   __builtin_amdgcn_sched_group_barrier(0x008, nm - (nm / nr) * nr, 0);
 }
 
-// offsets: p.offsets as a separate restrict argument, so that the compiler
-// reads it with scalar loads (no store of the kernel can alias it) instead of
-// vector loads whose waits would drain the loads in flight
+// offsets, counts: p.offsets and p.counts as separate restrict arguments, so
+// that the compiler reads them with scalar loads (no store of the kernel can
+// alias them) instead of vector loads whose waits would drain the loads in
+// flight
 __global__ __launch_bounds__(WgradTile::THREADS) void wgrad_kernel(BwdWgrad p,
-                                                                   const int32_t* __restrict__ offsets) {
+                                                                   const int32_t* __restrict__ offsets,
+                                                                   const int32_t* __restrict__ counts) {
   using TL = WgradTile;
   constexpr int NS = TL::NS;
   constexpr int NM = TL::MI * TL::NI / 2;  // MFMAs per phase
@@ -297,9 +299,9 @@ __global__ __launch_bounds__(WgradTile::THREADS) void wgrad_kernel(BwdWgrad p,
     b_off[i] = (uint32_t)(kr * p.x_row_bytes) + kload_col<TL::BN>(kr, lane);
   }
   const int64_t a_kstep = (int64_t)TL::BK * p.y_row_bytes, b_kstep = (int64_t)TL::BK * p.x_row_bytes;
-  // tile t: expert, output origin (m0 rows, n0 columns), K tiles (an even
-  // number: an expert's rows are padded to 64), and the wave-uniform bases
-  // of its Y and X columns
+  // tile t: expert, output origin (m0 rows, n0 columns), K tiles (over the
+  // expert's rows: a last K tile of the 64-row padding that holds no row is
+  // skipped), and the wave-uniform bases of its Y and X columns
   auto info = [&](int t, int& e, int& m0, int& n0, const char*& ya, const char*& xb) {
     e = t / per_e;
     const int r = t - e * per_e;
@@ -308,7 +310,8 @@ __global__ __launch_bounds__(WgradTile::THREADS) void wgrad_kernel(BwdWgrad p,
     const int row0 = offsets[e];
     ya = uniform_ptr(p.Y + (int64_t)row0 * p.y_row_bytes + p.y_col_bytes + (int64_t)n0 * 2);
     xb = uniform_ptr(p.X + (int64_t)row0 * p.x_row_bytes + p.x_col_bytes + (int64_t)m0 * 2);
-    return (offsets[e + 1] - row0) / TL::BK;
+    const int rows = max(min(counts[e], offsets[e + 1] - row0), 0);
+    return (rows + TL::BK - 1) / TL::BK;
   };
   // the load cursor: tile lt, K tile lk of its lkt
   int lt = t0, lk = 0, lkt = 0;
@@ -385,9 +388,14 @@ __global__ __launch_bounds__(WgradTile::THREADS) void wgrad_kernel(BwdWgrad p,
     const char* ya;
     const char* xb;
     const int kt = info(t, e, m0, n0, ya, xb);
-    for (int k = 0; k < kt; k += 2) {
+    int k = 0;
+    for (; k + 1 < kt; k += 2) {
       step(h0, h1);
       step(h1, h0);
+    }
+    if (k < kt) {  // an odd count: the next K tile's first half went into h1
+      step(h0, h1);
+      h0 = h1;
     }
     // output rows m0 + wn WN + ni 16 + (0..15), columns n0 + wm WM + (0..63):
     // lane l holds row (l & 15) of block ni, columns mi 16 + 4 (l >> 4) + (0..3)
@@ -441,7 +449,7 @@ hipError_t launch_bwd_wgrad(const BwdWgrad& p, hipStream_t s) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int64_t grid = std::min<int64_t>(pad8(tiles), std::max(8, cus / 8 * 8));
-  wgrad_kernel<<<(int)grid, WgradTile::THREADS, 0, s>>>(p, p.offsets);
+  wgrad_kernel<<<(int)grid, WgradTile::THREADS, 0, s>>>(p, p.offsets, p.counts);
   return hipGetLastError();
 }
 

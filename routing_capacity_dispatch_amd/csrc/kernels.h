@@ -251,7 +251,8 @@ struct BwdWgrad {
   int64_t x_row_bytes, x_col_bytes;
   const char* Y;          // K-major rows of the N operand
   int64_t y_row_bytes, y_col_bytes;
-  const int32_t* offsets;  // [E+1] padded: expert e contracts rows [offsets[e], offsets[e+1])
+  const int32_t* offsets;  // [E+1] padded: expert e's rows sit in [offsets[e], offsets[e+1])
+  const int32_t* counts;   // [E] rows of expert e; the rest of its padded range is zeros
   int E, M, N;
   int tiles_m, tiles_n;
   char* C;                // [E][M][N]

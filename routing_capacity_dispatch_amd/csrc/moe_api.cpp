@@ -1178,6 +1178,7 @@ moe_status run_experts_bwd(const moe_config* c, const moe_plan& p, const BwdRows
     w.y_row_bytes = yr;
     w.y_col_bytes = 0;
     w.offsets = offsets;
+    w.counts = counts;
     w.E = E;
     w.M = M;
     w.N = N;
