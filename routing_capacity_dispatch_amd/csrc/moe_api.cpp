@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int64_t kI32Max = 2147483647;
+constexpr int32_t kMaxWidth = 1 << 20;  // largest d_model, d_latent, d_ff, d_ff_shared
 
 // Stages of moe_forward, in launch order: latent GEMM, router GEMM, top-k,
 // slot assignment, row scatter, receiver binning, expert row lists, expert
@@ -121,6 +122,11 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
   if (c->d_model % 64 || c->d_latent % 64 || c->d_ff % 64 ||
       (c->n_shared > 0 && c->d_ff_shared % 64))
+    return MOE_ERR_UNSUPPORTED;
+  // widths up to 2^20: with T * k < 2^31 and every capacity product below
+  // 2^31, each workspace size below stays far inside int64
+  if (c->d_model > kMaxWidth || c->d_latent > kMaxWidth || c->d_ff > kMaxWidth ||
+      (c->n_shared > 0 && c->d_ff_shared > kMaxWidth))
     return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 3) return MOE_ERR_UNSUPPORTED;
   if (c->n_waves > 65535) return MOE_ERR_UNSUPPORTED;  // the slot scan's grid has one row per wave

@@ -121,11 +121,27 @@ def _status(fn):
     ("d_ff", 96, abi.MOE_ERR_UNSUPPORTED),
     ("n_shared", 4, abi.MOE_ERR_UNSUPPORTED),
     ("n_waves", 65536, abi.MOE_ERR_UNSUPPORTED),
+    # widths above 2^20 (multiples of 64): workspace sizes stay far inside int64
+    ("d_model", (1 << 20) + 64, abi.MOE_ERR_UNSUPPORTED),
+    ("d_latent", (1 << 20) + 64, abi.MOE_ERR_UNSUPPORTED),
+    ("d_ff", (1 << 30), abi.MOE_ERR_UNSUPPORTED),
+    ("d_ff_shared", (1 << 31) - 64, abi.MOE_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(lib, field, value, status):
     cfg = rcd.config_of(synth.workload("tiny_fp32"))
     setattr(cfg, field, value)
     assert _status(lambda: rcd.plan(cfg)) == status
+
+
+def test_widest_supported_fp32_plan_sizes(lib):
+    # the widest fp32 widths with a long T: every size positive and exact
+    # (no wrap-around), the shared hidden rows T * S * Fs * 4 bytes among them
+    T, wide = 1 << 20, 1 << 20
+    cfg = rcd.make_config(T, wide, wide, 64, 16, 8, wide, n_shared=3, d_ff_shared=wide, dtype="f32")
+    p = rcd.plan(cfg)
+    # z, y_latent and the shared hidden rows alone
+    assert p["forward_ws_bytes"] > 2 * T * wide * 4 + T * 3 * wide * 4
+    assert p["backward_ws_bytes"] > 0 and p["dropless_backward_ws_bytes"] > 0
 
 
 def test_too_many_experts_unsupported(lib):
