@@ -506,7 +506,7 @@ __global__ __launch_bounds__(TL::THREADS) void ragged_gemm_kernel(RaggedGemm p) 
           if (m0 + row < rows && c0 + col < p.F) {
             const float a = acc.v[mi][2 * q][r], b = acc.v[mi][2 * q + 1][r];
             const float dh = bf16_to_f32(*reinterpret_cast<const uint16_t*>(ldh + row * ld + col * 2));
-            const float sg = 1.0f / (1.0f + __expf(-a));
+            const float sg = sigmoid(a);
             const float sa = a * sg;
             da = dh * b * sg * (1.0f + a * (1.0f - sg));
             db = dh * sa;
