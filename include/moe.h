@@ -168,7 +168,8 @@ int32_t moe_version(void);
    W < 1, a factor with den <= 0 or num < 0), MOE_ERR_UNSUPPORTED
    (d_model, d_latent, d_ff or d_ff_shared not a multiple of 64 or above
    2^20, E > 1024, k > 64, n_shared > 3, n_waves > 65535, an index that would
-   not fit in int32, a bf16 operand buffer of 4 GiB or more). */
+   not fit in int32, a bf16 operand buffer of 4 GiB or more, a grouped GEMM
+   of more than 2^23 - 8 tiles). */
 moe_status moe_make_plan(const moe_config* cfg, moe_plan* plan);
 
 /* Router selection (ranhao.site section 2.2: top-8 routing with a balancing

@@ -15,6 +15,10 @@ namespace {
 
 constexpr int64_t kI32Max = 2147483647;
 constexpr int32_t kMaxWidth = 1 << 20;  // largest d_model, d_latent, d_ff, d_ff_shared
+// Most entries of a grouped GEMM's tile list: its grid (one 512-thread
+// workgroup per entry, rounded up to a multiple of 8) stays below 2^32
+// work-items.
+constexpr int64_t kMaxListEntries = (int64_t(1) << 23) - 8;
 
 // Stages of moe_forward, in launch order: latent GEMM, router GEMM, top-k,
 // slot assignment, row scatter, receiver binning, expert row lists, expert
@@ -178,7 +182,7 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   if (c->dtype == MOE_BF16) {
     int64_t e0, e1;
     capped_entries(c, W * cr, &e0, &e1);
-    if (e0 > kI32Max / 3 || e1 > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+    if (e0 > kMaxListEntries || e1 > kMaxListEntries) return MOE_ERR_UNSUPPORTED;
     x.take((E + 1) * 4);          // expert-major row offsets
     x.take(E * W * cr * 4);       // flat pool-row index of each kept row
     x.take(e0 * 12);              // gate/up tile list
@@ -215,7 +219,7 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   const int64_t n = T * k;
   int64_t ent0, ent1;
   dropless_entries(c, &ent0, &ent1);
-  if (ent0 > kI32Max / 3 || ent1 > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+  if (ent0 > kMaxListEntries || ent1 > kMaxListEntries) return MOE_ERR_UNSUPPORTED;
   const int64_t nblk = moe::ragged_sort_blocks(n);
   p->dropless_rows = n;
   Carver dd{nullptr, 0};
@@ -249,7 +253,8 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   const int64_t R = kept_max + 63 * E;
   int64_t bpre, bdh, bdu;
   backward_entries(c, R, &bpre, &bdh, &bdu);
-  if (R > kI32Max || bpre > kI32Max / 3 || bdh > kI32Max / 3 || bdu > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+  if (R > kI32Max || bpre > kMaxListEntries || bdh > kMaxListEntries || bdu > kMaxListEntries)
+    return MOE_ERR_UNSUPPORTED;
   p->backward_rows = R;
   Carver bx{nullptr, 0};
   bx.take(E * 4);           // rows per expert
@@ -269,7 +274,8 @@ moe_status plan_impl(const moe_config* c, moe_plan* p) {
   const int64_t Rd = n + 63 * E;
   int64_t dpre, ddh, ddu;
   backward_entries(c, Rd, &dpre, &ddh, &ddu);
-  if (Rd > kI32Max || dpre > kI32Max / 3 || ddh > kI32Max / 3 || ddu > kI32Max / 3) return MOE_ERR_UNSUPPORTED;
+  if (Rd > kI32Max || dpre > kMaxListEntries || ddh > kMaxListEntries || ddu > kMaxListEntries)
+    return MOE_ERR_UNSUPPORTED;
   p->dropless_backward_rows = Rd;
   Carver dbx{nullptr, 0};
   dbx.take(E * 4);

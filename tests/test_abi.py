@@ -134,14 +134,24 @@ def test_plan_rejects(lib, field, value, status):
 
 
 def test_widest_supported_fp32_plan_sizes(lib):
-    # the widest fp32 widths with a long T: every size positive and exact
-    # (no wrap-around), the shared hidden rows T * S * Fs * 4 bytes among them
-    T, wide = 1 << 20, 1 << 20
+    # the widest fp32 widths: every size positive and exact (no wrap-around),
+    # the shared hidden rows T * S * Fs * 4 bytes among them
+    T, wide = 1 << 14, 1 << 20
     cfg = rcd.make_config(T, wide, wide, 64, 16, 8, wide, n_shared=3, d_ff_shared=wide, dtype="f32")
     p = rcd.plan(cfg)
     # z, y_latent and the shared hidden rows alone
     assert p["forward_ws_bytes"] > 2 * T * wide * 4 + T * 3 * wide * 4
     assert p["backward_ws_bytes"] > 0 and p["dropless_backward_ws_bytes"] > 0
+
+
+def test_tile_lists_past_the_grid_limit_unsupported(lib):
+    # one 512-thread workgroup per tile of a grouped GEMM: a grid must stay
+    # below 2^32 work-items, so at most 2^23 - 8 tiles per list
+    wide = 1 << 20
+    ok = rcd.make_config(1 << 14, 64, 64, 64, 16, 8, wide, dtype="f32")
+    rcd.plan(ok)
+    big = rcd.make_config(1 << 16, 64, 64, 64, 16, 8, wide, dtype="f32")
+    assert _status(lambda: rcd.plan(big)) == abi.MOE_ERR_UNSUPPORTED
 
 
 def test_too_many_experts_unsupported(lib):
