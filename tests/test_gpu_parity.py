@@ -235,6 +235,47 @@ def test_experts(case):
     assert worst <= tol(dt), worst
 
 
+@pytest.mark.parametrize("dt,T,E,P,k,W,L,F", [("f32", 256, 16, 4, 2, 3, 128, 128),
+                                              ("bf16", 512, 8, 2, 2, 1, 256, 256)])
+def test_experts_saturating_preactivations(dt, T, E, P, k, W, L, F):
+    """Gate weights scaled by 200, so gate pre-activations reach |a| of several
+    hundred: the sigmoid's e^-a overflows to inf (its reciprocal 0, silu(a) a
+    signed zero) or underflows to 0 (silu(a) = a), and the experts' outputs
+    still match the fp64 SwiGLU row-wise."""
+    d = dev()
+    say("experts, saturating pre-activations", dt, T, E, P, k, W, L, F)
+    topk = synth.topk_case(T, E, k, seed=13, skew=0.0)
+    z = synth.rows_case(T, L, seed=14, dtype=dt)
+    wl = synth.Workload("x", T=T, d_model=64, d_latent=L, n_experts=E, n_pools=P, top_k=k,
+                        d_ff=F, n_shared=0, d_ff_shared=64, n_waves=W, dtype=dt, bias="zero")
+    ew = synth.expert_weights(wl, seed=6, device=d)
+    ew["w_gate"] = ew["w_gate"] * 200
+    cfg = rcd.make_config(T, 64, L, E, P, k, F, n_waves=W, dtype=dt)
+    dsp = rcd.dispatch(cfg, topk.to(d), z.to(d))
+    eo = rcd.experts(cfg, dsp["pools"], dsp["bank_rows"], dsp["expert_count"], ew["w_gate"],
+                     ew["w_up"], ew["w_down"])
+    torch.cuda.synchronize()
+    p = dsp["plan"]
+    ref = oracle.assign_slots(topk.numpy(), E, P, W, p["cap_send"], p["cap_recv"])
+    view = rcd.expert_out_view(cfg, eo)
+    Tw = p["tokens_per_wave"]
+    zf = f64(z)
+    worst, saturated = 0.0, 0
+    for e in range(E):
+        t_idx, j_idx = np.nonzero((topk.numpy() == e) & (ref["recv_slot"] >= 0))
+        if not len(t_idx):
+            continue
+        a = zf[t_idx] @ f64(ew["w_gate"][e]).T
+        saturated += int((np.abs(a) > 100).sum())
+        o = oracle.swiglu(zf[t_idx], f64(ew["w_gate"][e]), f64(ew["w_up"][e]), f64(ew["w_down"][e]))
+        got = f64(view[torch.from_numpy(t_idx // Tw).to(d), e // (E // P),
+                       torch.from_numpy(ref["pool_slot"][t_idx, j_idx]).to(d)])
+        assert np.isfinite(got).all()
+        worst = max(worst, rowwise_rel_err(got, o))
+    assert saturated > 1000, saturated  # the case reaches the saturated range
+    assert worst <= tol(dt), worst
+
+
 # ------------------------------------------------------------------ combine
 @pytest.mark.parametrize("dt,T,E,P,k,W,L", [("f32", 256, 16, 4, 2, 3, 128),
                                             ("bf16", 4096, 64, 16, 8, 3, 512),
